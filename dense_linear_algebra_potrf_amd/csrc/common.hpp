@@ -1,0 +1,182 @@
+// Shared device/host helpers for the batched potrf / posv kernels (gfx950).
+//
+// Element types are plain structs: complex numbers are interleaved (re, im)
+// pairs and every complex product is written out as real multiply-adds (the
+// BatchLAS perf_level3 page, section on register-tiled kernels, records that a
+// library complex multiply lowers to a slow runtime call and that accumulator
+// arrays must stay in registers).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <tuple>
+#include <type_traits>
+#include <utility>
+
+namespace bl {
+
+struct cfloat { float re, im; };
+struct cdouble { double re, im; };
+
+enum class DT : int { F32 = 0, F64 = 1, C64 = 2, C128 = 3 };
+
+template <typename T> struct Traits;
+template <> struct Traits<float>   { using R = float;  static constexpr bool cplx = false; static constexpr DT dt = DT::F32; };
+template <> struct Traits<double>  { using R = double; static constexpr bool cplx = false; static constexpr DT dt = DT::F64; };
+template <> struct Traits<cfloat>  { using R = float;  static constexpr bool cplx = true;  static constexpr DT dt = DT::C64; };
+template <> struct Traits<cdouble> { using R = double; static constexpr bool cplx = true;  static constexpr DT dt = DT::C128; };
+
+inline int elem_bytes(DT dt) {
+    switch (dt) {
+    case DT::F32: return 4;
+    case DT::F64: return 8;
+    case DT::C64: return 8;
+    case DT::C128: return 16;
+    }
+    return 0;
+}
+
+// ---------------------------------------------------------------- scalars
+template <typename T> __device__ __forceinline__ T zero() { return T{}; }
+template <typename T> __device__ __forceinline__ T one() {
+    if constexpr (Traits<T>::cplx) return T{1, 0};
+    else return T(1);
+}
+template <typename T> __device__ __forceinline__ typename Traits<T>::R re(const T& x) {
+    if constexpr (Traits<T>::cplx) return x.re;
+    else return x;
+}
+template <typename T> __device__ __forceinline__ T conj(const T& x) {
+    if constexpr (Traits<T>::cplx) return T{x.re, -x.im};
+    else return x;
+}
+template <typename T> __device__ __forceinline__ T from_real(typename Traits<T>::R v) {
+    if constexpr (Traits<T>::cplx) return T{v, 0};
+    else return v;
+}
+// Real diagonal value whose conjugate has imaginary part +0 (Upper stores conj).
+template <typename T> __device__ __forceinline__ T diag_value(typename Traits<T>::R v, bool conj_on_store) {
+    using R = typename Traits<T>::R;
+    if constexpr (Traits<T>::cplx) return T{v, conj_on_store ? R(-0.0) : R(0.0)};
+    else return v;
+}
+template <typename T> __device__ __forceinline__ T scale(const T& x, typename Traits<T>::R s) {
+    if constexpr (Traits<T>::cplx) return T{x.re * s, x.im * s};
+    else return x * s;
+}
+template <typename T> __device__ __forceinline__ T select(bool c, const T& a, const T& b) {
+    // component-wise select: keeps aggregates in registers
+    if constexpr (Traits<T>::cplx) return T{c ? a.re : b.re, c ? a.im : b.im};
+    else return c ? a : b;
+}
+// acc -= t * conj(c)
+template <typename T> __device__ __forceinline__ void sub_mul_conj(T& acc, const T& t, const T& c) {
+    if constexpr (Traits<T>::cplx) {
+        acc.re = __builtin_fma(-t.re, c.re, __builtin_fma(-t.im, c.im, acc.re));
+        acc.im = __builtin_fma(-t.im, c.re, __builtin_fma(t.re, c.im, acc.im));
+    } else {
+        acc = __builtin_fma(-t, c, acc);
+    }
+}
+// acc -= t * c
+template <typename T> __device__ __forceinline__ void sub_mul(T& acc, const T& t, const T& c) {
+    if constexpr (Traits<T>::cplx) {
+        acc.re = __builtin_fma(-t.re, c.re, __builtin_fma(t.im, c.im, acc.re));
+        acc.im = __builtin_fma(-t.re, c.im, __builtin_fma(-t.im, c.re, acc.im));
+    } else {
+        acc = __builtin_fma(-t, c, acc);
+    }
+}
+// acc -= conj(t) * c
+template <typename T> __device__ __forceinline__ void sub_conj_mul(T& acc, const T& t, const T& c) {
+    if constexpr (Traits<T>::cplx) {
+        acc.re = __builtin_fma(-t.re, c.re, __builtin_fma(-t.im, c.im, acc.re));
+        acc.im = __builtin_fma(-t.re, c.im, __builtin_fma(t.im, c.re, acc.im));
+    } else {
+        acc = __builtin_fma(-t, c, acc);
+    }
+}
+
+// Reciprocal, reciprocal square root and square root of a positive pivot.
+// float: the hardware approximations (about 1 ulp), well inside the 1e-4
+// parity tolerance.  double: correctly rounded library operations, because the
+// fp64 hardware approximations are far less accurate than 1e-11.
+__device__ __forceinline__ float pivot_rcp(float d) { return __builtin_amdgcn_rcpf(d); }
+__device__ __forceinline__ float pivot_rsq(float d) { return __builtin_amdgcn_rsqf(d); }
+__device__ __forceinline__ float pivot_sqrt(float d) { return __builtin_amdgcn_sqrtf(d); }
+__device__ __forceinline__ double pivot_rcp(double d) { return 1.0 / d; }
+__device__ __forceinline__ double pivot_sqrt(double d) { return __builtin_sqrt(d); }
+__device__ __forceinline__ double pivot_rsq(double d) { return 1.0 / __builtin_sqrt(d); }
+
+// ---------------------------------------------------------------- compile-time loops
+template <int V> using ic = std::integral_constant<int, V>;
+
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(ic<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for_down(F&& f) {   // E-1 down to B
+    if constexpr (B < E) {
+        f(ic<E - 1>{});
+        static_for_down<B, E - 1>(f);
+    }
+}
+
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- LDS element access
+// Elements are stored as D = sizeof(T)/4 consecutive dwords.
+template <typename T> constexpr int words() { return int(sizeof(T) / 4); }
+
+template <typename T>
+__device__ __forceinline__ void lds_put(uint32_t* base, int idx, const T& v) {
+    *reinterpret_cast<T*>(base + idx * words<T>()) = v;
+}
+template <typename T>
+__device__ __forceinline__ T lds_get(const uint32_t* base, int idx) {
+    return *reinterpret_cast<const T*>(base + idx * words<T>());
+}
+template <typename T>
+__device__ __forceinline__ T from_words(const uint32_t* w) {
+    T v;
+    __builtin_memcpy(&v, w, sizeof(T));
+    return v;
+}
+
+// Ordering of LDS traffic between lanes of one wavefront: LDS instructions of a
+// wave execute in order, so only the compiler has to be kept from reordering.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------- host launch helper
+namespace detail {
+template <typename Tuple, size_t... I>
+inline hipError_t launch_tuple(const void* fn, dim3 g, dim3 b, size_t shm, hipStream_t s, Tuple& t,
+                               std::index_sequence<I...>) {
+    void* args[] = {static_cast<void*>(&std::get<I>(t))..., nullptr};
+    return hipLaunchKernel(fn, g, b, args, shm, s);
+}
+}  // namespace detail
+
+// Launch a __global__ function and return the launch's own error code.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*fn)(KArgs...), dim3 grid, dim3 block, size_t shm, hipStream_t s,
+                         Args... args) {
+    std::tuple<KArgs...> t(static_cast<KArgs>(args)...);
+    return detail::launch_tuple(reinterpret_cast<const void*>(fn), grid, block, shm, s, t,
+                                std::index_sequence_for<KArgs...>{});
+}
+
+}  // namespace bl

@@ -1,0 +1,30 @@
+// Families that are not built yet: they report that they cannot run anything,
+// so the dispatcher never routes to them and a pin returns NOT_SUPPORTED.
+#include "families.hpp"
+
+namespace bl {
+
+int posv_tiny_max_n(DT) { return 0; }
+int posv_tiny_max_nrhs() { return 0; }
+bool posv_tiny_geometry(DT, int, int, int64_t, Geometry&) { return false; }
+hipError_t posv_tiny(DT, bool, int, int, void*, int64_t, int64_t, void*, int64_t, int64_t, int64_t,
+                     int32_t*, hipStream_t) { return hipErrorNotSupported; }
+
+int lds_max_n(DT) { return 0; }
+bool lds_geometry(DT, int, int64_t, Geometry&) { return false; }
+hipError_t lds_potrf(DT, bool, int, void*, int64_t, int64_t, int64_t, int32_t*, hipStream_t) {
+    return hipErrorNotSupported;
+}
+
+bool blocked_supported(DT, int) { return false; }
+bool blocked_geometry(DT, int, int64_t, Geometry&) { return false; }
+hipError_t blocked_potrf(DT, bool, int, void*, int64_t, int64_t, int64_t, int32_t*, hipStream_t) {
+    return hipErrorNotSupported;
+}
+
+int potrs_max_nrhs() { return 0; }
+bool potrs_supported(DT, int, int) { return false; }
+hipError_t potrs(DT, bool, int, int, const void*, int64_t, int64_t, void*, int64_t, int64_t, int64_t,
+                 const int32_t*, hipStream_t) { return hipErrorNotSupported; }
+
+}  // namespace bl

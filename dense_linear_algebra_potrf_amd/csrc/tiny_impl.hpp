@@ -1,0 +1,222 @@
+// Tiny family (implementation header): batched Cholesky with each matrix held in registers.
+//
+// Prior art: the BatchLAS perf_potrf page, section "potrf: the tiny tier" (one
+// matrix per lane partition, lane r owns row r, every value stays in
+// registers) and section "The shared tiny-tier invariants" (no dynamic
+// register indexing, failure writes as selects, every lane of a partition
+// reaches every exchange, dead slots load the identity, Upper as a load/store
+// transform).  That design targets 32-wide sub-groups; this one is built for
+// 64-wide wavefronts:
+//
+//   * A matrix is owned by a partition of P lanes; lane q holds rows
+//     q, q + P, ..., q + (R-1) P (R rows per lane), so a partition serves
+//     orders n <= P R and a wavefront packs G = floor(64 / P) matrices.  P need
+//     not be a power of two (n = 17 runs as 7 matrices of 9 lanes x 2 rows).
+//   * Row block r only ever needs columns < (r + 1) P, so the triangular
+//     shape of the work is kept: block 0 stops updating early.
+//   * The pivot column is exchanged through LDS: each lane writes its entry of
+//     column j once and every lane reads the column back with 16-byte
+//     broadcast reads (the pages replaced per-element shuffles the same way,
+//     section "The posv local-memory transpose").  The buffer is double
+//     buffered by step parity, so no barrier is needed inside a wavefront.
+//   * The rank-1 update uses the unscaled column: s_ik -= (s_ij / d) s_kj^H,
+//     with d the updated (never stale) Schur pivot; the scaled factor column
+//     l_ij = s_ij / sqrt(d) is written back afterwards.
+//   * Failure handling follows the pages' info contract: d fails when
+//     !(d > 0); the first failing column is kept and later updates stop
+//     (section "potrf: correctness findings", item 6).
+#pragma once
+
+#include "families.hpp"
+
+namespace bl {
+namespace tiny_detail {
+
+constexpr int kTinyWaves = 4;   // wavefronts per workgroup, each independent
+
+// Dwords per partition row of the column buffer: >= nb * D, of the form
+// 32 m + 4, so partitions of a wave start on different 16-byte bank groups.
+constexpr int tiny_row_words(int nb, int d) {
+    int w = nb * d;
+    int m = (w - 4 + 31) / 32;
+    if (m < 0) m = 0;
+    return 32 * m + 4;
+}
+
+template <typename T, int P, int R, bool UPPER>
+__global__ __launch_bounds__(64 * kTinyWaves) void potrf_tiny_kernel(
+    T* __restrict__ A, int n, int64_t lda, int64_t stride, int64_t batch,
+    int32_t* __restrict__ info)
+{
+    using Rt = typename Traits<T>::R;
+    constexpr int NB = P * R;
+    constexpr int G = 64 / P;
+    constexpr int PARTS = 63 / P + 1;     // includes a partial, dead tail partition
+    constexpr int D = words<T>();
+    constexpr int ROWW = tiny_row_words(NB, D);
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kTinyWaves][2][PARTS][ROWW];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int p = lane / P;
+    const int q = lane - p * P;
+    const int64_t b = ((int64_t)blockIdx.x * kTinyWaves + wave) * G + p;
+    const bool live = (p < G) && (b < batch);
+    T* __restrict__ Ab = A + (live ? b : 0) * stride;
+
+    // S(i, c) for c <= i: A(i, c) for Lower, conj(A(c, i)) for Upper.  Rows at
+    // or beyond n, and dead partitions, hold the identity.
+    T a[R][NB];
+    static_for<0, R>([&](auto rr) {
+        constexpr int r = rr;
+        const int i = q + r * P;
+        const bool row_ok = live && i < n;
+        static_for<0, cmin(NB, (r + 1) * P)>([&](auto cc) {
+            constexpr int c = cc;
+            T v = (i == c) ? one<T>() : zero<T>();
+            if (row_ok && c <= i) {
+                if constexpr (UPPER) v = conj(Ab[c + (int64_t)i * lda]);
+                else v = Ab[i + (int64_t)c * lda];
+            }
+            a[r][c] = v;
+        });
+    });
+
+    int32_t inf = 0;
+    bool alive = true;
+    static_for<0, NB>([&](auto jj) {
+        constexpr int j = jj;
+        if (j < n) {
+            constexpr int rj = j / P;
+            uint32_t* row = &lds[wave][j & 1][p][0];
+            static_for<rj, R>([&](auto rr) {
+                constexpr int r = rr;
+                lds_put<T>(row, q + r * P, a[r][j]);
+            });
+            wave_lds_sync();
+            uint32_t w[ROWW];
+            constexpr int v0 = (j * D) / 4;
+            constexpr int v1 = cdiv(NB * D, 4);
+            static_for<v0, v1>([&](auto vv) {
+                constexpr int v = vv;
+                const uint4 x = reinterpret_cast<const uint4*>(row)[v];
+                w[4 * v + 0] = x.x;
+                w[4 * v + 1] = x.y;
+                w[4 * v + 2] = x.z;
+                w[4 * v + 3] = x.w;
+            });
+            const Rt d = re(from_words<T>(&w[j * D]));
+            const bool bad = !(d > Rt(0));
+            inf = (alive && bad) ? (j + 1) : inf;
+            alive = alive && !bad;
+            const Rt inv = pivot_rcp(d);
+            const Rt rs = pivot_rsq(d);
+            const Rt sq = pivot_sqrt(d);
+            static_for<rj, R>([&](auto rr) {
+                constexpr int r = rr;
+                constexpr int kend = cmin(NB, (r + 1) * P);
+                const int i = q + r * P;
+                const bool below = alive && (i > j);
+                const T t = select(below, scale(a[r][j], inv), zero<T>());
+                static_for<j + 1, kend>([&](auto kk) {
+                    constexpr int k = kk;
+                    sub_mul_conj(a[r][k], t, from_words<T>(&w[k * D]));
+                });
+                const T fin = select(i == j, diag_value<T>(sq, UPPER), scale(a[r][j], rs));
+                a[r][j] = select(alive && i >= j, fin, a[r][j]);
+            });
+        }
+    });
+
+    static_for<0, R>([&](auto rr) {
+        constexpr int r = rr;
+        const int i = q + r * P;
+        const bool row_ok = live && i < n;
+        static_for<0, cmin(NB, (r + 1) * P)>([&](auto cc) {
+            constexpr int c = cc;
+            if (row_ok && c <= i) {
+                if constexpr (UPPER) Ab[c + (int64_t)i * lda] = conj(a[r][c]);
+                else Ab[i + (int64_t)c * lda] = a[r][c];
+            }
+        });
+    });
+    if (live && q == 0 && info != nullptr) info[b] = inf;
+}
+
+// ---------------------------------------------------------------- configurations
+template <int P_, int R_> struct TC {
+    static constexpr int P = P_, R = R_, NB = P_ * R_;
+};
+template <typename... Cs> struct TList {};
+
+// Ordered by order served (NB); the first entry with NB >= n is used.
+template <typename T> struct TinyConfigs;
+template <> struct TinyConfigs<float> {
+    using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<9, 2>, TC<8, 3>, TC<8, 4>,
+                       TC<11, 3>>;
+};
+template <> struct TinyConfigs<double> {
+    using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<8, 3>, TC<8, 4>>;
+};
+template <> struct TinyConfigs<cfloat> {
+    using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<8, 3>, TC<8, 4>>;
+};
+template <> struct TinyConfigs<cdouble> {
+    using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>>;
+};
+
+template <typename F, typename C, typename... Cs>
+bool pick_config(TList<C, Cs...>, int n, F&& f) {
+    if (n <= C::NB) {
+        f(C{});
+        return true;
+    }
+    if constexpr (sizeof...(Cs) > 0) return pick_config(TList<Cs...>{}, n, f);
+    else return false;
+}
+
+template <typename C, typename... Cs>
+constexpr int last_nb(TList<C, Cs...>) {
+    if constexpr (sizeof...(Cs) > 0) return last_nb(TList<Cs...>{});
+    else return C::NB;
+}
+
+template <typename T>
+bool geometry_t(int n, int64_t batch, Geometry& g) {
+    return pick_config(typename TinyConfigs<T>::type{}, n, [&](auto c) {
+        using C = decltype(c);
+        constexpr int G = 64 / C::P;
+        constexpr int D = words<T>();
+        g.family = FAM_TINY;
+        g.P = C::P;
+        g.R = C::R;
+        g.G = G;
+        g.threads = 64 * kTinyWaves;
+        g.panel = 0;
+        g.grid = (batch + G * kTinyWaves - 1) / (G * kTinyWaves);
+        g.lds = int64_t(kTinyWaves) * 2 * (63 / C::P + 1) * tiny_row_words(C::NB, D) * 4;
+    });
+}
+
+template <typename T>
+hipError_t potrf_t(bool upper, int n, void* A, int64_t lda, int64_t stride, int64_t batch,
+                   int32_t* info, hipStream_t s) {
+    hipError_t err = hipErrorInvalidValue;
+    pick_config(typename TinyConfigs<T>::type{}, n, [&](auto c) {
+        using C = decltype(c);
+        constexpr int G = 64 / C::P;
+        const int64_t grid = (batch + G * kTinyWaves - 1) / (G * kTinyWaves);
+        const dim3 gd((unsigned)grid), bd(64 * kTinyWaves);
+        T* a = static_cast<T*>(A);
+        if (upper)
+            err = launch(potrf_tiny_kernel<T, C::P, C::R, true>, gd, bd, 0, s, a, n, lda, stride,
+                         batch, info);
+        else
+            err = launch(potrf_tiny_kernel<T, C::P, C::R, false>, gd, bd, 0, s, a, n, lda, stride,
+                         batch, info);
+    });
+    return err;
+}
+
+}  // namespace tiny_detail
+}  // namespace bl

@@ -1,0 +1,141 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+validates arguments in the documented order before touching the GPU, and its
+host-only route query agrees with the families' tables.  Also the build gate:
+no kernel uses scratch memory."""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import dense_linear_algebra_potrf_amd as bl
+from dense_linear_algebra_potrf_amd import build as blbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "batchlas.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bl.LIB_PATH):
+        blbuild.build(incremental=True, verbose=False)
+    return bl.load_library()
+
+
+def declared_functions() -> set[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(batchlas_[a-z_]+)\s*\(", text))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert names == set(bl.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", bl.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (batchlas_\w+)", out))
+    assert names <= exported
+
+
+def test_version_and_status_strings(lib):
+    assert lib.batchlas_version() >= 100
+    for code in range(6):
+        assert lib.batchlas_status_string(code)
+    assert lib.batchlas_status_string(99) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    (dict(n=0), 1, "n must be"),
+    (dict(n=-3), 1, "n must be"),
+    (dict(batch=0), 1, "batch must be"),
+    (dict(lda=7), 1, "lda must be"),
+    (dict(stride=63), 1, "strideA"),
+    (dict(A=None), 2, "A is NULL"),
+    (dict(dt=7), 1, "dtype"),
+    (dict(uplo=2), 1, "uplo"),
+    (dict(stride=1 << 62, batch=1 << 10), 1, "overflows"),
+    # order: n is checked before lda, lda before the pointer
+    (dict(n=0, lda=0, A=None), 1, "n must be"),
+    (dict(lda=1, A=None), 1, "lda must be"),
+])
+def test_potrf_validation(lib, args, status, msg):
+    a = dict(dt=0, uplo=0, n=8, A=FAKE, lda=8, stride=64, batch=4)
+    a.update(args)
+    st = lib.batchlas_potrf(a["dt"], a["uplo"], a["n"], a["A"], a["lda"], a["stride"], a["batch"],
+                            None, None)
+    assert st == status
+    assert msg in lib.batchlas_last_error().decode()
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    (dict(nrhs=0), 1, "nrhs must be"),
+    (dict(ldb=3), 1, "ldb must be"),
+    (dict(strideB=15), 1, "strideB"),
+    (dict(B=None), 2, "B is NULL"),
+])
+def test_posv_validation(lib, args, status, msg):
+    a = dict(dt=0, uplo=0, n=8, nrhs=2, A=FAKE, lda=8, strideA=64, B=FAKE, ldb=8, strideB=16,
+             batch=4)
+    a.update(args)
+    st = lib.batchlas_posv(a["dt"], a["uplo"], a["n"], a["nrhs"], a["A"], a["lda"], a["strideA"],
+                           a["B"], a["ldb"], a["strideB"], a["batch"], None, None)
+    assert st == status
+    assert msg in lib.batchlas_last_error().decode()
+
+
+def test_unknown_family_is_rejected(lib):
+    st = lib.batchlas_potrf_family(42, 0, 0, 8, FAKE, 8, 64, 4, None, None)
+    assert st == 1
+
+
+def test_route_tiny_geometry_invariants(lib):
+    for dt in ("f32", "f64", "c64", "c128"):
+        for n in range(1, 34):
+            try:
+                r = bl.route(dt, "L", n, 1000, family="tiny")
+            except bl.BatchlasError as e:
+                assert e.status_name == "NOT_SUPPORTED"
+                continue
+            P, R, G = r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]
+            assert P * R >= n and G == 64 // P and G >= 1
+            assert r["grid"] * G * (r["block_threads"] // 64) >= 1000
+            assert r["family"] == "tiny"
+
+
+def test_route_auto_picks_by_size(lib):
+    assert bl.route("f32", "L", 8, 1024)["family"] == "tiny"
+    assert bl.route("f32", "L", 17, 32768)["family"] == "tiny"
+    assert bl.route("c128", "U", 16, 64)["family"] == "tiny"
+
+
+def _route_in_subprocess(env_extra: dict, code: str) -> str:
+    env = dict(os.environ, **env_extra)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                         cwd=ROOT)
+    return out.stdout.strip() + out.stderr.strip()
+
+
+def test_environment_pin_is_read_and_a_bad_pin_is_an_error(lib):
+    code = ("import dense_linear_algebra_potrf_amd as bl\n"
+            "try:\n    print(bl.route('f32','L',8,64)['family'])\n"
+            "except bl.BatchlasError as e:\n    print('ERR', e)\n")
+    assert _route_in_subprocess({"BATCHLAS_POTRF_ROUTE": "tiny"}, code).endswith("tiny")
+    res = _route_in_subprocess({"BATCHLAS_POTRF_ROUTE": "native:tiny"}, code)
+    assert "ERR INVALID_VALUE" in res and "does not parse" in res
+
+
+def test_no_kernel_uses_scratch(lib):
+    res = json.load(open(blbuild.RESOURCES))
+    assert res, "resource report is empty"
+    bad = {k: v for k, v in res.items() if v.get("scratch_bytes", 0) != 0}
+    assert not bad, f"kernels with scratch (dynamic register indexing?): {sorted(bad)}"
