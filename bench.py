@@ -1,0 +1,304 @@
+"""Benchmark for batched potrf / posv on one MI355X.
+
+`python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-secondary]`
+
+A step is one call of the library on one batch of synthetic input that is
+already resident in HBM.  Since potrf works in place, every step gets its own
+freshly prepared copy of the input (copies are made before the timed region,
+and together they exceed the 256 MB MALL, so each step starts from HBM).
+W untimed steps, then exactly K timed steps bracketed by synchronisation; rank
+0 prints ONE JSON line.
+
+The headline workload is fp32 Lower potrf, n = 33, batch 16384 (matrices/s,
+HBM GB/s and its fraction of the 8 TB/s peak).  Secondary lines cover the
+other workloads (n = 8, 17; posv n = 32 nrhs = 4; complex-float Upper n = 64;
+fp64 n = 512 in GFLOP/s against the 78.6 TFLOP/s FP64 peak).
+
+The roofline of the dominant kernel uses the algorithmic bytes (or flops) of
+one launch divided by the launch's average duration, measured with HIP events
+on the stream the kernel runs on.  The CPU baseline times the oracle on the
+host cores on a bounded sample of the same workload.
+
+Modes for profiling: --mode copy runs a plain device copy of known size (the
+calibration for FETCH_SIZE / WRITE_SIZE counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "batched potrf matrices/s + GB/s (% HBM peak) fp32 n=33; GFLOP/s fp64 n=512"
+
+CONFIGS = {
+    "potrf_f32_L_n8_b1024": dict(op="potrf", dt="f32", uplo="L", n=8, batch=1024, seed=1001, plant=64),
+    "potrf_f32_L_n8_b1048576": dict(op="potrf", dt="f32", uplo="L", n=8, batch=1 << 20, seed=1011, plant=64),
+    "potrf_f32_L_n17_b32768": dict(op="potrf", dt="f32", uplo="L", n=17, batch=32768, seed=1021),
+    "potrf_f32_L_n33_b16384": dict(op="potrf", dt="f32", uplo="L", n=33, batch=16384, seed=1022),
+    "posv_f32_L_n32_r4_b16384": dict(op="posv", dt="f32", uplo="L", n=32, nrhs=4, batch=16384, seed=1003),
+    "potrf_c64_U_n64_b16384": dict(op="potrf", dt="c64", uplo="U", n=64, batch=16384, seed=1004),
+    "potrf_f64_L_n512_b1024": dict(op="potrf", dt="f64", uplo="L", n=512, batch=1024, seed=1005),
+}
+PRIMARY = "potrf_f32_L_n33_b16384"
+SECONDARY = ["potrf_f32_L_n17_b32768", "potrf_f32_L_n8_b1024", "potrf_f32_L_n8_b1048576",
+             "posv_f32_L_n32_r4_b16384", "potrf_c64_U_n64_b16384", "potrf_f64_L_n512_b1024"]
+
+
+def describe(cfg: dict) -> str:
+    kind = {"f32": "s", "f64": "d", "c64": "c", "c128": "z"}[cfg["dt"]] + cfg["op"]
+    s = f"{kind} {'lower' if cfg['uplo'] == 'L' else 'upper'} n={cfg['n']}"
+    if cfg["op"] == "posv":
+        s += f" nrhs={cfg['nrhs']}"
+    return s + f" batch={cfg['batch']}, column-major lda=n stride=n*n, A = G G^H/n + I (seed {cfg['seed']})"
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_linear_algebra_potrf_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def make_input(cfg: dict):
+    """Host buffers (column-major) for a workload."""
+    import numpy as np
+    import synthetic as syn
+    a = syn.spd_matrices(cfg["n"], cfg["batch"], cfg["dt"], cfg["seed"],
+                         chunk=64 if cfg["n"] >= 128 else 4096)
+    if cfg.get("plant"):
+        syn.plant_failures(a, cfg["seed"], every=cfg["plant"])
+    abuf = syn.to_colmajor(a)
+    del a
+    bbuf = None
+    if cfg["op"] == "posv":
+        bbuf = syn.to_colmajor(syn.rhs(cfg["n"], cfg["nrhs"], cfg["batch"], cfg["dt"], cfg["seed"]))
+    return abuf, bbuf
+
+
+def bench_config(name: str, steps: int, warmup: int) -> dict:
+    import torch
+    import dense_linear_algebra_potrf_amd as bl
+    from dense_linear_algebra_potrf_amd import metrics
+
+    cfg = CONFIGS[name]
+    abuf, bbuf = make_input(cfg)
+    dev = torch.device("cuda:0")
+    pa = torch.from_numpy(abuf).to(dev)
+    pb = torch.from_numpy(bbuf).to(dev) if bbuf is not None else None
+    n, batch, dt, uplo = cfg["n"], cfg["batch"], cfg["dt"], cfg["uplo"]
+    nrhs = cfg.get("nrhs", 0)
+    # one fresh copy per step (potrf works in place); then a 1 GiB flush so that
+    # the timed steps start from HBM, not from the 256 MB MALL or the L2s
+    per_copy = pa.numel() * pa.element_size() + (pb.numel() * pb.element_size() if pb is not None else 0)
+    if (steps + warmup) * per_copy > (96 << 30):
+        raise SystemExit(f"{name}: {steps + warmup} copies of {per_copy >> 20} MiB do not fit")
+    work_a = [pa.clone() for _ in range(steps + warmup)]
+    work_b = [pb.clone() for _ in range(steps + warmup)] if pb is not None else None
+    info = torch.empty(batch, dtype=torch.int32, device=dev)
+    route = bl.route(dt, uplo, n, batch, nrhs=nrhs)
+    stream = torch.cuda.current_stream()
+
+    def launch(i):
+        if cfg["op"] == "potrf":
+            bl.potrf(work_a[i], uplo, info, n=n, batch=batch)
+        else:
+            bl.posv(work_a[i], work_b[i], uplo, info, n=n, nrhs=nrhs, batch=batch)
+
+    for k in range(warmup):
+        launch(k)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush.fill_(7)
+    del flush
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ev0[k].record(stream)
+        launch(warmup + k)
+        ev1[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [ev0[k].elapsed_time(ev1[k]) for k in range(steps)]
+    # correctness guard on the last step: info must be as planted
+    info_h = info.cpu().numpy()
+    if cfg.get("plant"):
+        bad = int((info_h != 0).sum())
+        expect = len(range(0, batch, cfg["plant"]))
+        assert bad == expect, f"{name}: {bad} failed items, expected {expect}"
+    else:
+        assert (info_h == 0).all(), f"{name}: unexpected info"
+
+    ms_step = wall * 1e3 / steps
+    ms_kernel = sum(kern_ms) / steps
+    if cfg["op"] == "potrf":
+        byts = metrics.potrf_bytes(n, batch, dt, uplo)
+        flops = metrics.potrf_flops(n, dt) * batch
+    else:
+        byts = metrics.posv_bytes(n, nrhs, batch, dt, uplo)
+        flops = metrics.posv_flops(n, nrhs, dt) * batch
+    peak_tf = metrics.PEAK_TFLOPS[dt]
+    res = {
+        "workload": describe(cfg),
+        "family": route["family"],
+        "geometry": {k: route[k] for k in ("lanes_per_matrix", "rows_per_lane", "matrices_per_wave",
+                                           "block_threads", "panel", "grid")},
+        "ms_per_step": ms_step,
+        "ms_per_call_events": ms_kernel,
+        "matrices_per_s": batch / (ms_step * 1e-3),
+        "gflops": flops / (ms_step * 1e-3) / 1e9,
+        "gbs": byts / (ms_step * 1e-3) / 1e9,
+        "hbm_frac": byts / (ms_step * 1e-3) / 1e9 / metrics.HBM_PEAK_GBS,
+        "flop_frac": flops / (ms_step * 1e-3) / 1e12 / peak_tf,
+        "alg_bytes_per_call": byts,
+        "alg_flops_per_call": flops,
+    }
+    # roofline of the dominant kernel (one launch per call for the single-launch families)
+    bound = "mfma" if (dt in ("f64", "c128") and n >= 256) else "hbm"
+    if bound == "hbm":
+        ach = byts / (ms_kernel * 1e-3) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": metrics.HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": ach / metrics.HBM_PEAK_GBS,
+                           "traffic": None}
+    else:
+        ach = flops / (ms_kernel * 1e-3) / 1e12
+        res["roofline"] = {"bound": "mfma", "achieved": ach, "peak": peak_tf, "unit": "TFLOP/s",
+                           "frac": ach / peak_tf, "traffic": None}
+    del work_a, work_b, pa, pb
+    torch.cuda.empty_cache()
+    return res
+
+
+def attach_traffic(name: str, res: dict) -> None:
+    """HBM traffic per launch from committed counter runs, if the kernels are unchanged."""
+    path = os.path.join(ROOT, "profiles", f"{name}.counters.json")
+    if not os.path.exists(path):
+        return
+    rec = json.load(open(path))
+    if rec.get("source_digest") != source_digest():
+        return
+    res["roofline"]["traffic"] = rec.get("traffic_bytes")
+
+
+def cpu_baseline(name: str, budget_s: float = 1.5) -> dict:
+    """The oracle on the host cores, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    cfg = CONFIGS[name]
+    threads = max(1, min(16, os.cpu_count() or 1))
+    n, dt = cfg["n"], cfg["dt"]
+    per = max(1, min(cfg["batch"], int(2e8 // max(1, n ** 3))))   # first sample size
+    sample = dict(cfg, batch=per)
+    abuf, bbuf = make_input(sample)
+    done, t = 0, 0.0
+    while t < budget_s and done < 64 * cfg["batch"]:
+        a = abuf.copy()
+        b = bbuf.copy() if bbuf is not None else None
+        t0 = time.perf_counter()
+        if cfg["op"] == "potrf":
+            oracle.potrf(a, cfg["uplo"], n, per, nthreads=threads)
+        else:
+            oracle.posv(a, b, cfg["uplo"], n, cfg["nrhs"], per, nthreads=threads)
+        t += time.perf_counter() - t0
+        done += per
+    return {"value": done / t, "unit": "matrices/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} matrices ({per} per pass) of: {describe(cfg)}; "
+                      f"{t:.2f} s wall on {threads} threads"}
+
+
+def copy_mode(mib: int, reps: int) -> None:
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy", "bytes_each_way": mib << 20, "reps": reps}))
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=PRIMARY, choices=sorted(CONFIGS))
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the batched factorisation has no cross-GPU step, "
+              "so only --gpus 1 is supported (a batch shards by slicing it across GPUs).",
+              file=sys.stderr)
+        return 2
+    if a.mode == "copy":
+        copy_mode(a.copy_mib, max(1, a.steps))
+        return 0
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    import dense_linear_algebra_potrf_amd as bl
+    bl.load_library()
+
+    prim = bench_config(a.config, a.steps, a.warmup)
+    attach_traffic(a.config, prim)
+    cfg = CONFIGS[a.config]
+    out = {
+        "metric": METRIC,
+        "value": prim["matrices_per_s"],
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": prim["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dt"],
+        "data": "synthetic",
+        "config": {"workload": prim["workload"], "op": cfg["op"], "n": cfg["n"], "batch": cfg["batch"],
+                   "uplo": cfg["uplo"], "family": prim["family"], "parallelism": "batch on 1 GPU"},
+        "gbs": prim["gbs"],
+        "hbm_frac": prim["hbm_frac"],
+        "gflops": prim["gflops"],
+        "roofline": prim["roofline"],
+    }
+    if not a.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(a.config)
+    if not a.no_secondary:
+        sec = {}
+        for name in SECONDARY:
+            if name == a.config:
+                continue
+            c = CONFIGS[name]
+            try:
+                bl.route(c["dt"], c["uplo"], c["n"], c["batch"], nrhs=c.get("nrhs", 0))
+            except bl.BatchlasError as e:
+                sec[name] = {"skipped": str(e)}
+                continue
+            r = bench_config(name, max(3, min(a.steps, 10)), max(1, min(a.warmup, 3)))
+            attach_traffic(name, r)
+            sec[name] = r
+            print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step, {r['gbs']:.0f} GB/s, "
+                  f"{r['gflops']:.0f} GFLOP/s", file=sys.stderr, flush=True)
+        out["secondary"] = sec
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

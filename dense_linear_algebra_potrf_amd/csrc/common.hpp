@@ -71,31 +71,36 @@ template <typename T> __device__ __forceinline__ T select(bool c, const T& a, co
     if constexpr (Traits<T>::cplx) return T{c ? a.re : b.re, c ? a.im : b.im};
     else return c ? a : b;
 }
+// Fused multiply-add in the element's own precision (__builtin_fma is the
+// double-precision builtin; float needs __builtin_fmaf).
+__device__ __forceinline__ float fmadd(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ __forceinline__ double fmadd(double a, double b, double c) { return __builtin_fma(a, b, c); }
+
 // acc -= t * conj(c)
 template <typename T> __device__ __forceinline__ void sub_mul_conj(T& acc, const T& t, const T& c) {
     if constexpr (Traits<T>::cplx) {
-        acc.re = __builtin_fma(-t.re, c.re, __builtin_fma(-t.im, c.im, acc.re));
-        acc.im = __builtin_fma(-t.im, c.re, __builtin_fma(t.re, c.im, acc.im));
+        acc.re = fmadd(-t.re, c.re, fmadd(-t.im, c.im, acc.re));
+        acc.im = fmadd(-t.im, c.re, fmadd(t.re, c.im, acc.im));
     } else {
-        acc = __builtin_fma(-t, c, acc);
+        acc = fmadd(-t, c, acc);
     }
 }
 // acc -= t * c
 template <typename T> __device__ __forceinline__ void sub_mul(T& acc, const T& t, const T& c) {
     if constexpr (Traits<T>::cplx) {
-        acc.re = __builtin_fma(-t.re, c.re, __builtin_fma(t.im, c.im, acc.re));
-        acc.im = __builtin_fma(-t.re, c.im, __builtin_fma(-t.im, c.re, acc.im));
+        acc.re = fmadd(-t.re, c.re, fmadd(t.im, c.im, acc.re));
+        acc.im = fmadd(-t.re, c.im, fmadd(-t.im, c.re, acc.im));
     } else {
-        acc = __builtin_fma(-t, c, acc);
+        acc = fmadd(-t, c, acc);
     }
 }
 // acc -= conj(t) * c
 template <typename T> __device__ __forceinline__ void sub_conj_mul(T& acc, const T& t, const T& c) {
     if constexpr (Traits<T>::cplx) {
-        acc.re = __builtin_fma(-t.re, c.re, __builtin_fma(-t.im, c.im, acc.re));
-        acc.im = __builtin_fma(-t.re, c.im, __builtin_fma(t.im, c.re, acc.im));
+        acc.re = fmadd(-t.re, c.re, fmadd(-t.im, c.im, acc.re));
+        acc.im = fmadd(-t.re, c.im, fmadd(t.im, c.re, acc.im));
     } else {
-        acc = __builtin_fma(-t, c, acc);
+        acc = fmadd(-t, c, acc);
     }
 }
 
@@ -158,6 +163,43 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------- buffer memory access
+// Raw buffer loads/stores with a 32-bit byte offset from a wave-uniform base.
+// An offset at or above 2^31 is outside the descriptor's range: the load
+// returns zero and the store is dropped, without touching memory.  This gives
+// branch-free predication that never reads or writes masked elements.
+constexpr uint32_t kBufOOB = 0x80000000u;
+constexpr int kBufFlags = 0x00020000;   // gfx9-family descriptor word 3 (raw, dword data)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, kBufFlags);
+}
+
+template <typename T>
+__device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    } else if constexpr (sizeof(T) == 8) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    } else {
+        static_assert(sizeof(T) == 16, "element size");
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off, const T& v) {
+    if constexpr (sizeof(T) == 4) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+    } else if constexpr (sizeof(T) == 8) {
+        using V = uint32_t __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(V, v), r, off, 0, 0);
+    } else {
+        using V = uint32_t __attribute__((ext_vector_type(4)));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(V, v), r, off, 0, 0);
+    }
 }
 
 // ---------------------------------------------------------------- host launch helper

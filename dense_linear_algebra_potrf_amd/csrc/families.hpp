@@ -32,6 +32,7 @@ struct Geometry {
 
 // --- tiny: registers, P lanes x R rows per matrix, 64/P matrices per wavefront
 int tiny_max_n(DT dt);
+bool tiny_layout_ok(DT dt, int n, int64_t stride);   // byte offsets of a wave fit in 31 bits
 bool tiny_geometry(DT dt, int n, int64_t batch, Geometry& g);
 hipError_t tiny_potrf(DT dt, bool upper, int n, void* A, int64_t lda, int64_t stride,
                       int64_t batch, int32_t* info, hipStream_t s);

@@ -6,6 +6,7 @@ namespace bl {
 #define BL_DECLARE_TINY(suf)                                                                  \
     int tiny_max_n_##suf();                                                                   \
     bool tiny_geometry_##suf(int n, int64_t batch, Geometry& g);                              \
+    bool tiny_layout_ok_##suf(int n, int64_t stride);                                         \
     hipError_t tiny_potrf_##suf(bool upper, int n, void* A, int64_t lda, int64_t stride,      \
                                 int64_t batch, int32_t* info, hipStream_t s);
 BL_DECLARE_TINY(f32)
@@ -22,6 +23,16 @@ int tiny_max_n(DT dt) {
     case DT::C128: return tiny_max_n_c128();
     }
     return 0;
+}
+
+bool tiny_layout_ok(DT dt, int n, int64_t stride) {
+    switch (dt) {
+    case DT::F32: return tiny_layout_ok_f32(n, stride);
+    case DT::F64: return tiny_layout_ok_f64(n, stride);
+    case DT::C64: return tiny_layout_ok_c64(n, stride);
+    case DT::C128: return tiny_layout_ok_c128(n, stride);
+    }
+    return false;
 }
 
 bool tiny_geometry(DT dt, int n, int64_t batch, Geometry& g) {

@@ -6,6 +6,8 @@ namespace bl {
 
 int tiny_max_n_c128() { return tiny_detail::last_nb(tiny_detail::TinyConfigs<cdouble>::type{}); }
 
+bool tiny_layout_ok_c128(int n, int64_t stride) { return tiny_detail::layout_ok_t<cdouble>(n, stride); }
+
 bool tiny_geometry_c128(int n, int64_t batch, Geometry& g) {
     return tiny_detail::geometry_t<cdouble>(n, batch, g);
 }

@@ -6,6 +6,8 @@ namespace bl {
 
 int tiny_max_n_c64() { return tiny_detail::last_nb(tiny_detail::TinyConfigs<cfloat>::type{}); }
 
+bool tiny_layout_ok_c64(int n, int64_t stride) { return tiny_detail::layout_ok_t<cfloat>(n, stride); }
+
 bool tiny_geometry_c64(int n, int64_t batch, Geometry& g) {
     return tiny_detail::geometry_t<cfloat>(n, batch, g);
 }

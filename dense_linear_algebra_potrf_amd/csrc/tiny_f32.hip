@@ -6,6 +6,8 @@ namespace bl {
 
 int tiny_max_n_f32() { return tiny_detail::last_nb(tiny_detail::TinyConfigs<float>::type{}); }
 
+bool tiny_layout_ok_f32(int n, int64_t stride) { return tiny_detail::layout_ok_t<float>(n, stride); }
+
 bool tiny_geometry_f32(int n, int64_t batch, Geometry& g) {
     return tiny_detail::geometry_t<float>(n, batch, g);
 }

@@ -6,6 +6,8 @@ namespace bl {
 
 int tiny_max_n_f64() { return tiny_detail::last_nb(tiny_detail::TinyConfigs<double>::type{}); }
 
+bool tiny_layout_ok_f64(int n, int64_t stride) { return tiny_detail::layout_ok_t<double>(n, stride); }
+
 bool tiny_geometry_f64(int n, int64_t batch, Geometry& g) {
     return tiny_detail::geometry_t<double>(n, batch, g);
 }

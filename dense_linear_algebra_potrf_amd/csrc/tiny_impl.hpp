@@ -37,7 +37,7 @@ constexpr int kTinyWaves = 4;   // wavefronts per workgroup, each independent
 // Dwords per partition row of the column buffer: >= nb * D, of the form
 // 32 m + 4, so partitions of a wave start on different 16-byte bank groups.
 constexpr int tiny_row_words(int nb, int d) {
-    int w = nb * d;
+    int w = (nb + 1) * d;   // one spare slot
     int m = (w - 4 + 31) / 32;
     if (m < 0) m = 0;
     return 32 * m + 4;
@@ -57,12 +57,29 @@ __global__ __launch_bounds__(64 * kTinyWaves) void potrf_tiny_kernel(
     __shared__ __attribute__((aligned(16))) uint32_t lds[kTinyWaves][2][PARTS][ROWW];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int p = lane / P;
     const int q = lane - p * P;
-    const int64_t b = ((int64_t)blockIdx.x * kTinyWaves + wave) * G + p;
+    const int64_t b_first = ((int64_t)blockIdx.x * kTinyWaves + wave) * G;   // wave-uniform
+    const int64_t b = b_first + p;
     const bool live = (p < G) && (b < batch);
-    T* __restrict__ Ab = A + (live ? b : 0) * stride;
+    // One buffer descriptor per wavefront; the host guarantees every byte offset
+    // inside the wave's G matrices is below 2^31.  Masked elements use an
+    // out-of-range offset, so they are neither read nor written.
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(A + b_first * stride);
+    constexpr uint32_t S = sizeof(T);
+    const uint32_t lda_b = uint32_t(lda) * S;
+    uint32_t roff[R];
+    static_for<0, R>([&](auto rr) {
+        constexpr int r = rr;
+        const int i = q + r * P;
+        const uint32_t base = UPPER ? uint32_t(p * stride + int64_t(i) * lda) * S
+                                    : uint32_t(p * stride + i) * S;
+        roff[r] = (live && i < n) ? base : kBufOOB;
+    });
+    auto elem_off = [&](int r, int c) -> uint32_t {
+        return UPPER ? roff[r] + uint32_t(c) * S : roff[r] + uint32_t(c) * lda_b;
+    };
 
     // S(i, c) for c <= i: A(i, c) for Lower, conj(A(c, i)) for Upper.  Rows at
     // or beyond n, and dead partitions, hold the identity.
@@ -70,60 +87,107 @@ __global__ __launch_bounds__(64 * kTinyWaves) void potrf_tiny_kernel(
     static_for<0, R>([&](auto rr) {
         constexpr int r = rr;
         const int i = q + r * P;
-        const bool row_ok = live && i < n;
         static_for<0, cmin(NB, (r + 1) * P)>([&](auto cc) {
             constexpr int c = cc;
-            T v = (i == c) ? one<T>() : zero<T>();
-            if (row_ok && c <= i) {
-                if constexpr (UPPER) v = conj(Ab[c + (int64_t)i * lda]);
-                else v = Ab[i + (int64_t)c * lda];
-            }
+            uint32_t off = elem_off(r, c);
+            if constexpr (c >= r * P) off = (c <= i) ? off : kBufOOB;   // diagonal block
+            T v = buf_load<T>(rsrc, off);
+            if constexpr (UPPER) v = conj(v);
+            if constexpr (c >= r * P) v = select(c == i && roff[r] == kBufOOB, one<T>(), v);
             a[r][c] = v;
         });
     });
 
+    // Register slots a[r][k] with k > i (the row's upper part) are scratch: they
+    // absorb updates but never feed a referenced slot, so a step needs no
+    // per-row guards.  Rows at or beyond n hold the identity, so every one of
+    // the NB steps can run unconditionally: a padding step sees d = 1 and
+    // leaves the referenced part alone.  After a failed pivot the recurrence
+    // continues (NaN from the failing column on); the leading columns are final
+    // by then and info keeps the first failing column.
+    //
+    // Look-ahead: within step j, column j+1 is updated first and published to
+    // LDS, and its 16-byte broadcast reads are issued before the rest of step
+    // j's updates, so the exchange latency hides behind that arithmetic.
+    // Column j is published at slots relative to j (row i -> slot i - j), so
+    // the entries a step needs always start at slot 0: 16-byte aligned reads,
+    // fewer of them as j grows.  Rows above j write to a spare slot at NB.
+    auto publish = [&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int rj = j / P;
+        uint32_t* row = &lds[wave][j & 1][p][0];
+        static_for<rj, R>([&](auto rr) {
+            constexpr int r = rr;
+            const int i = q + r * P;
+            const int slot = (r == rj) ? ((i >= j) ? i - j : NB) : i - j;
+            lds_put<T>(row, slot, a[r][j]);
+        });
+    };
+    auto fetch = [&](auto jc, uint32_t (&w)[ROWW]) {
+        constexpr int j = decltype(jc)::value;
+        const uint4* row4 = reinterpret_cast<const uint4*>(
+            __builtin_assume_aligned(&lds[wave][j & 1][p][0], 16));
+        static_for<0, cdiv((NB - j) * D, 4)>([&](auto vv) {
+            constexpr int v = vv;
+            const uint4 x = row4[v];
+            w[4 * v + 0] = x.x;
+            w[4 * v + 1] = x.y;
+            w[4 * v + 2] = x.z;
+            w[4 * v + 3] = x.w;
+        });
+    };
+    // entry for row k of column j (k >= j) in a fetched column
+    auto colv = [&](const uint32_t (&w)[ROWW], int j, int k) -> T {
+        return from_words<T>(&w[(k - j) * D]);
+    };
+
     int32_t inf = 0;
-    bool alive = true;
+    uint32_t wcur[ROWW];
+    publish(ic<0>{});
+    wave_lds_sync();
+    fetch(ic<0>{}, wcur);
     static_for<0, NB>([&](auto jj) {
         constexpr int j = jj;
-        if (j < n) {
-            constexpr int rj = j / P;
-            uint32_t* row = &lds[wave][j & 1][p][0];
-            static_for<rj, R>([&](auto rr) {
+        constexpr int rj = j / P;
+        const Rt d = re(colv(wcur, j, j));
+        inf = (inf == 0 && !(d > Rt(0))) ? (j + 1) : inf;
+        const Rt inv = pivot_rcp(d);
+        const Rt rs = pivot_rsq(d);
+        T t[R];
+        static_for<rj, R>([&](auto rr) {
+            constexpr int r = rr;
+            t[r] = scale(a[r][j], inv);
+        });
+        uint32_t wnext[ROWW];
+        if constexpr (j + 1 < NB) {
+            constexpr int rn = (j + 1) / P;
+            static_for<rn, R>([&](auto rr) {
                 constexpr int r = rr;
-                lds_put<T>(row, q + r * P, a[r][j]);
+                sub_mul_conj(a[r][j + 1], t[r], colv(wcur, j, j + 1));
             });
+            publish(ic<j + 1>{});
             wave_lds_sync();
-            uint32_t w[ROWW];
-            constexpr int v0 = (j * D) / 4;
-            constexpr int v1 = cdiv(NB * D, 4);
-            static_for<v0, v1>([&](auto vv) {
-                constexpr int v = vv;
-                const uint4 x = reinterpret_cast<const uint4*>(row)[v];
-                w[4 * v + 0] = x.x;
-                w[4 * v + 1] = x.y;
-                w[4 * v + 2] = x.z;
-                w[4 * v + 3] = x.w;
+            fetch(ic<j + 1>{}, wnext);
+        }
+        static_for<rj, R>([&](auto rr) {
+            constexpr int r = rr;
+            constexpr int kend = cmin(NB, (r + 1) * P);
+            static_for<j + 2, kend>([&](auto kk) {
+                constexpr int k = kk;
+                sub_mul_conj(a[r][k], t[r], colv(wcur, j, k));
             });
-            const Rt d = re(from_words<T>(&w[j * D]));
-            const bool bad = !(d > Rt(0));
-            inf = (alive && bad) ? (j + 1) : inf;
-            alive = alive && !bad;
-            const Rt inv = pivot_rcp(d);
-            const Rt rs = pivot_rsq(d);
-            const Rt sq = pivot_sqrt(d);
-            static_for<rj, R>([&](auto rr) {
-                constexpr int r = rr;
-                constexpr int kend = cmin(NB, (r + 1) * P);
-                const int i = q + r * P;
-                const bool below = alive && (i > j);
-                const T t = select(below, scale(a[r][j], inv), zero<T>());
-                static_for<j + 1, kend>([&](auto kk) {
-                    constexpr int k = kk;
-                    sub_mul_conj(a[r][k], t, from_words<T>(&w[k * D]));
-                });
-                const T fin = select(i == j, diag_value<T>(sq, UPPER), scale(a[r][j], rs));
-                a[r][j] = select(alive && i >= j, fin, a[r][j]);
+            if constexpr (r == rj) {
+                // the one row block that holds row j itself
+                const bool diag = (q + r * P) == j;
+                a[r][j] = select(diag, diag_value<T>(pivot_sqrt(d), UPPER), scale(a[r][j], rs));
+            } else {
+                a[r][j] = scale(a[r][j], rs);
+            }
+        });
+        if constexpr (j + 1 < NB) {
+            static_for<0, 4 * cdiv((NB - j - 1) * D, 4)>([&](auto kk) {
+                constexpr int k = kk;
+                wcur[k] = wnext[k];
             });
         }
     });
@@ -131,13 +195,12 @@ __global__ __launch_bounds__(64 * kTinyWaves) void potrf_tiny_kernel(
     static_for<0, R>([&](auto rr) {
         constexpr int r = rr;
         const int i = q + r * P;
-        const bool row_ok = live && i < n;
         static_for<0, cmin(NB, (r + 1) * P)>([&](auto cc) {
             constexpr int c = cc;
-            if (row_ok && c <= i) {
-                if constexpr (UPPER) Ab[c + (int64_t)i * lda] = conj(a[r][c]);
-                else Ab[i + (int64_t)c * lda] = a[r][c];
-            }
+            uint32_t off = elem_off(r, c);
+            if constexpr (c >= r * P) off = (c <= i) ? off : kBufOOB;
+            if constexpr (UPPER) buf_store<T>(rsrc, off, conj(a[r][c]));
+            else buf_store<T>(rsrc, off, a[r][c]);
         });
     });
     if (live && q == 0 && info != nullptr) info[b] = inf;
@@ -179,6 +242,19 @@ template <typename C, typename... Cs>
 constexpr int last_nb(TList<C, Cs...>) {
     if constexpr (sizeof...(Cs) > 0) return last_nb(TList<Cs...>{});
     else return C::NB;
+}
+
+// The wave's G matrices must lie within 2^31 bytes of the wave's base, so the
+// 32-bit buffer offsets (and the out-of-range mask) are exact.
+template <typename T>
+bool layout_ok_t(int n, int64_t stride) {
+    bool ok = false;
+    pick_config(typename TinyConfigs<T>::type{}, n, [&](auto c) {
+        using C = decltype(c);
+        constexpr int64_t G = 64 / C::P;
+        ok = stride <= (int64_t(0x7fffffff) / int64_t(sizeof(T))) / G;
+    });
+    return ok;
 }
 
 template <typename T>
