@@ -203,7 +203,8 @@ batchlas_status route_posv(int requested, DT dt, int n, int nrhs, int64_t stride
                                                     "' does not parse (auto|tiny|split)");
         fam = e.posv_pin;
     }
-    const bool tiny_ok = n <= bl::posv_tiny_max_n(dt) && nrhs <= bl::posv_tiny_max_nrhs();
+    const bool tiny_ok = n <= bl::posv_tiny_max_n(dt) && nrhs <= bl::posv_tiny_max_nrhs() &&
+                         bl::posv_tiny_layout_ok(dt, n, strideA, strideB);
     if (fam == bl::FAM_AUTO) fam = tiny_ok ? bl::FAM_POSV_TINY : bl::FAM_POSV_SPLIT;
     if (fam == bl::FAM_POSV_TINY) {
         if (!tiny_ok)

@@ -4,12 +4,6 @@
 
 namespace bl {
 
-int posv_tiny_max_n(DT) { return 0; }
-int posv_tiny_max_nrhs() { return 0; }
-bool posv_tiny_geometry(DT, int, int, int64_t, Geometry&) { return false; }
-hipError_t posv_tiny(DT, bool, int, int, void*, int64_t, int64_t, void*, int64_t, int64_t, int64_t,
-                     int32_t*, hipStream_t) { return hipErrorNotSupported; }
-
 int lds_max_n(DT) { return 0; }
 bool lds_geometry(DT, int, int64_t, Geometry&) { return false; }
 hipError_t lds_potrf(DT, bool, int, void*, int64_t, int64_t, int64_t, int32_t*, hipStream_t) {

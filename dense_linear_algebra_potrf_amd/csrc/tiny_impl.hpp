@@ -43,17 +43,122 @@ constexpr int tiny_row_words(int nb, int d) {
     return 32 * m + 4;
 }
 
-template <typename T, int P, int R, bool UPPER>
+// Forward solve L y = b and backward solve L^H x = y for the rows a lane holds
+// (the perf_potrf page, section "The fused posv tier", and section "posv: the
+// backward solve costs a transpose").  The forward solve is column-oriented:
+// once y_p is final its owner broadcasts it and every later row subtracts
+// L(i, p) y_p.  The backward solve needs column p of L, which no lane holds;
+// instead, at step p the owner of row p publishes that row through LDS and
+// each lane reads the one entry L(p, i) it needs.  B is written only when the
+// factorisation succeeded (info == 0), so a failed item leaves B unchanged.
+template <typename T, int P, int R, int NRHS>
+__device__ __forceinline__ void tiny_solves(const T (&a)[R][P * R], const typename Traits<T>::R (&invd)[R],
+                                            uint32_t* ldsw, int parity_words, int roww, int p, int q,
+                                            bool live, int n, int32_t inf, T* Bw, int nrhs,
+                                            int64_t ldb, int64_t strideB)
+{
+    constexpr int NB = P * R;
+    constexpr uint32_t S = sizeof(T);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bw);
+    const uint32_t ldb_b = uint32_t(ldb) * S;
+    uint32_t boff[R];
+    static_for<0, R>([&](auto rr) {
+        constexpr int r = rr;
+        const int i = q + r * P;
+        boff[r] = (live && i < n) ? uint32_t(p * strideB + i) * S : kBufOOB;
+    });
+    T y[R][NRHS];      // running right-hand sides
+    T yf[R][NRHS];     // final y of the held rows
+    static_for<0, R>([&](auto rr) {
+        static_for<0, NRHS>([&](auto kk) {
+            constexpr int r = rr, k = kk;
+            const uint32_t off = (k < nrhs) ? boff[r] + uint32_t(k) * ldb_b : kBufOOB;
+            y[r][k] = buf_load<T>(rb, off);
+            yf[r][k] = zero<T>();
+        });
+    });
+    // forward: L y = b, p ascending
+    static_for<0, NB>([&](auto pp) {
+        constexpr int pv = pp;
+        constexpr int rp = pv / P;
+        uint32_t* row = ldsw + (pv & 1) * parity_words + p * roww;
+        const bool owner = q == pv % P;
+        static_for<0, NRHS>([&](auto kk) {
+            constexpr int k = kk;
+            const T v = scale(y[rp][k], invd[rp]);
+            yf[rp][k] = select(owner, v, yf[rp][k]);
+            if (owner) lds_put<T>(row, NB + 1 + k, v);
+        });
+        wave_lds_sync();
+        T yp[NRHS];
+        static_for<0, NRHS>([&](auto kk) { yp[kk] = lds_get<T>(row, NB + 1 + kk); });
+        static_for<rp, R>([&](auto rr) {
+            constexpr int r = rr;
+            static_for<0, NRHS>([&](auto kk) {
+                constexpr int k = kk;
+                sub_mul(y[r][k], a[r][pv], yp[k]);
+            });
+        });
+    });
+    // backward: L^H x = y, p descending
+    T x[R][NRHS];
+    static_for<0, R>([&](auto rr) {
+        static_for<0, NRHS>([&](auto kk) { x[rr][kk] = yf[rr][kk]; });
+    });
+    T xf[R][NRHS];
+    static_for<0, R>([&](auto rr) {
+        static_for<0, NRHS>([&](auto kk) { xf[rr][kk] = zero<T>(); });
+    });
+    static_for_down<0, NB>([&](auto pp) {
+        constexpr int pv = pp;
+        constexpr int rp = pv / P;
+        uint32_t* row = ldsw + (pv & 1) * parity_words + p * roww;
+        const bool owner = q == pv % P;
+        static_for<0, NRHS>([&](auto kk) {
+            constexpr int k = kk;
+            const T v = scale(x[rp][k], invd[rp]);
+            xf[rp][k] = select(owner, v, xf[rp][k]);
+            if (owner) lds_put<T>(row, NB + 1 + k, v);
+        });
+        if (owner) {
+            static_for<0, pv>([&](auto cc) { lds_put<T>(row, cc, a[rp][cc]); });
+        }
+        wave_lds_sync();
+        T xp[NRHS];
+        static_for<0, NRHS>([&](auto kk) { xp[kk] = lds_get<T>(row, NB + 1 + kk); });
+        // rows below p (i < p) take conj(L(p, i)) x_p; other rows only absorb junk
+        static_for<0, cmin(R, rp + 1)>([&](auto rr) {
+            constexpr int r = rr;
+            const int i = q + r * P;
+            const T lpi = lds_get<T>(row, i < pv ? i : NB);
+            static_for<0, NRHS>([&](auto kk) {
+                constexpr int k = kk;
+                sub_conj_mul(x[r][k], lpi, xp[k]);
+            });
+        });
+    });
+    static_for<0, R>([&](auto rr) {
+        static_for<0, NRHS>([&](auto kk) {
+            constexpr int r = rr, k = kk;
+            const uint32_t off = (inf == 0 && k < nrhs) ? boff[r] + uint32_t(k) * ldb_b : kBufOOB;
+            buf_store<T>(rb, off, xf[r][k]);
+        });
+    });
+}
+
+// NRHS = 0: potrf.  NRHS > 0: posv for up to NRHS right-hand sides (nrhs at
+// run time), with the factor kept in registers for both triangular solves.
+template <typename T, int P, int R, bool UPPER, int NRHS>
 __global__ __launch_bounds__(64 * kTinyWaves) void potrf_tiny_kernel(
     T* __restrict__ A, int n, int64_t lda, int64_t stride, int64_t batch,
-    int32_t* __restrict__ info)
+    int32_t* __restrict__ info, T* __restrict__ B, int nrhs, int64_t ldb, int64_t strideB)
 {
     using Rt = typename Traits<T>::R;
     constexpr int NB = P * R;
     constexpr int G = 64 / P;
     constexpr int PARTS = 63 / P + 1;     // includes a partial, dead tail partition
     constexpr int D = words<T>();
-    constexpr int ROWW = tiny_row_words(NB, D);
+    constexpr int ROWW = tiny_row_words(NB + NRHS, D);
     __shared__ __attribute__((aligned(16))) uint32_t lds[kTinyWaves][2][PARTS][ROWW];
 
     const int lane = threadIdx.x & 63;
@@ -142,6 +247,8 @@ __global__ __launch_bounds__(64 * kTinyWaves) void potrf_tiny_kernel(
     };
 
     int32_t inf = 0;
+    Rt invd[R];                 // 1 / L(i, i) of each held row (used by the solves)
+    static_for<0, R>([&](auto rr) { invd[rr] = Rt(1); });
     uint32_t wcur[ROWW];
     publish(ic<0>{});
     wave_lds_sync();
@@ -180,6 +287,7 @@ __global__ __launch_bounds__(64 * kTinyWaves) void potrf_tiny_kernel(
                 // the one row block that holds row j itself
                 const bool diag = (q + r * P) == j;
                 a[r][j] = select(diag, diag_value<T>(pivot_sqrt(d), UPPER), scale(a[r][j], rs));
+                if constexpr (NRHS > 0) invd[r] = diag ? rs : invd[r];
             } else {
                 a[r][j] = scale(a[r][j], rs);
             }
@@ -191,6 +299,10 @@ __global__ __launch_bounds__(64 * kTinyWaves) void potrf_tiny_kernel(
             });
         }
     });
+
+    if constexpr (NRHS > 0)
+        tiny_solves<T, P, R, NRHS>(a, invd, &lds[wave][0][0][0], PARTS * ROWW, ROWW, p, q, live, n,
+                                   inf, B + b_first * strideB, nrhs, ldb, strideB);
 
     static_for<0, R>([&](auto rr) {
         constexpr int r = rr;
@@ -228,6 +340,16 @@ template <> struct TinyConfigs<cdouble> {
     using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>>;
 };
 
+// posv keeps more per lane (both solves' right-hand sides): smaller windows for
+// the double types so that nothing spills.
+template <typename T> struct PosvConfigs { using type = typename TinyConfigs<T>::type; };
+template <> struct PosvConfigs<double> {
+    using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<8, 3>>;
+};
+template <> struct PosvConfigs<cdouble> {
+    using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>>;
+};
+
 template <typename F, typename C, typename... Cs>
 bool pick_config(TList<C, Cs...>, int n, F&& f) {
     if (n <= C::NB) {
@@ -257,9 +379,9 @@ bool layout_ok_t(int n, int64_t stride) {
     return ok;
 }
 
-template <typename T>
+template <typename T, typename List = typename TinyConfigs<T>::type>
 bool geometry_t(int n, int64_t batch, Geometry& g) {
-    return pick_config(typename TinyConfigs<T>::type{}, n, [&](auto c) {
+    return pick_config(List{}, n, [&](auto c) {
         using C = decltype(c);
         constexpr int G = 64 / C::P;
         constexpr int D = words<T>();
@@ -284,12 +406,53 @@ hipError_t potrf_t(bool upper, int n, void* A, int64_t lda, int64_t stride, int6
         const int64_t grid = (batch + G * kTinyWaves - 1) / (G * kTinyWaves);
         const dim3 gd((unsigned)grid), bd(64 * kTinyWaves);
         T* a = static_cast<T*>(A);
+        T* nob = nullptr;
         if (upper)
-            err = launch(potrf_tiny_kernel<T, C::P, C::R, true>, gd, bd, 0, s, a, n, lda, stride,
-                         batch, info);
+            err = launch(potrf_tiny_kernel<T, C::P, C::R, true, 0>, gd, bd, 0, s, a, n, lda, stride,
+                         batch, info, nob, 0, int64_t(0), int64_t(0));
         else
-            err = launch(potrf_tiny_kernel<T, C::P, C::R, false>, gd, bd, 0, s, a, n, lda, stride,
-                         batch, info);
+            err = launch(potrf_tiny_kernel<T, C::P, C::R, false, 0>, gd, bd, 0, s, a, n, lda, stride,
+                         batch, info, nob, 0, int64_t(0), int64_t(0));
+    });
+    return err;
+}
+
+// posv: right-hand-side buckets NRHS = 1 and 4 (nrhs 2..4 run in the 4 bucket)
+constexpr int kPosvMaxRhs = 4;
+
+template <typename T>
+bool posv_layout_ok_t(int n, int64_t strideA, int64_t strideB) {
+    bool ok = false;
+    pick_config(typename PosvConfigs<T>::type{}, n, [&](auto c) {
+        using C = decltype(c);
+        constexpr int64_t G = 64 / C::P;
+        const int64_t lim = (int64_t(0x7fffffff) / int64_t(sizeof(T))) / G;
+        ok = strideA <= lim && strideB <= lim;
+    });
+    return ok;
+}
+
+template <typename T>
+hipError_t posv_t(bool upper, int n, int nrhs, void* A, int64_t lda, int64_t strideA, void* B,
+                  int64_t ldb, int64_t strideB, int64_t batch, int32_t* info, hipStream_t s) {
+    hipError_t err = hipErrorInvalidValue;
+    pick_config(typename PosvConfigs<T>::type{}, n, [&](auto c) {
+        using C = decltype(c);
+        constexpr int G = 64 / C::P;
+        const int64_t grid = (batch + G * kTinyWaves - 1) / (G * kTinyWaves);
+        const dim3 gd((unsigned)grid), bd(64 * kTinyWaves);
+        T* a = static_cast<T*>(A);
+        T* bb = static_cast<T*>(B);
+        auto go = [&](auto kern) {
+            err = launch(kern, gd, bd, 0, s, a, n, lda, strideA, batch, info, bb, nrhs, ldb, strideB);
+        };
+        if (nrhs == 1) {
+            if (upper) go(potrf_tiny_kernel<T, C::P, C::R, true, 1>);
+            else go(potrf_tiny_kernel<T, C::P, C::R, false, 1>);
+        } else {
+            if (upper) go(potrf_tiny_kernel<T, C::P, C::R, true, kPosvMaxRhs>);
+            else go(potrf_tiny_kernel<T, C::P, C::R, false, kPosvMaxRhs>);
+        }
     });
     return err;
 }
