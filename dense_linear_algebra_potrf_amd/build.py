@@ -47,8 +47,17 @@ def _sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _headers() -> list[str]:
-    return glob.glob(os.path.join(CSRC, "*.hpp")) + [os.path.join(ROOT, "include", "batchlas.h")]
+def _deps(src: str, seen: set | None = None) -> set:
+    """The source and every local header it includes, transitively."""
+    seen = set() if seen is None else seen
+    if src in seen or not os.path.exists(src):
+        return seen
+    seen.add(src)
+    for line in open(src, errors="replace"):
+        m = re.match(r'\s*#\s*include\s+"([^"]+)"', line)
+        if m:
+            _deps(os.path.normpath(os.path.join(os.path.dirname(src), m.group(1))), seen)
+    return seen
 
 
 def _obj(src: str) -> str:
@@ -59,7 +68,7 @@ def _compile(src: str, incremental: bool) -> tuple[str, str]:
     obj = _obj(src)
     rep = obj + ".res.txt"
     if incremental and os.path.exists(obj) and os.path.exists(rep):
-        newest = max(os.path.getmtime(p) for p in [src, *_headers()])
+        newest = max(os.path.getmtime(p) for p in _deps(src))
         if os.path.getmtime(obj) >= newest:
             return src, open(rep).read()
     cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj + ".tmp"]

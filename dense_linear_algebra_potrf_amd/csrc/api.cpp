@@ -144,25 +144,25 @@ batchlas_status check_common(int dt, int uplo, int64_t n, int64_t nrhs, bool is_
 }
 
 // ---------------------------------------------------------------- routing
-bool family_can_run_potrf(int fam, DT dt, int n, int64_t stride) {
+bool family_can_run_potrf(int fam, DT dt, int n, int64_t lda, int64_t stride) {
     switch (fam) {
     case bl::FAM_TINY: return n <= bl::tiny_max_n(dt) && bl::tiny_layout_ok(dt, n, stride);
     case bl::FAM_LDS: return n <= bl::lds_max_n(dt);
-    case bl::FAM_BLOCKED: return bl::blocked_supported(dt, n);
+    case bl::FAM_BLOCKED: return bl::blocked_supported(dt, n, lda);
     }
     return false;
 }
 
-int auto_potrf_family(DT dt, int n, int64_t stride) {
-    const bool tiny = family_can_run_potrf(bl::FAM_TINY, dt, n, stride);
+int auto_potrf_family(DT dt, int n, int64_t lda, int64_t stride) {
+    const bool tiny = family_can_run_potrf(bl::FAM_TINY, dt, n, lda, stride);
     if (tiny && n <= auto_tiny_cut(dt)) return bl::FAM_TINY;
-    if (family_can_run_potrf(bl::FAM_LDS, dt, n, stride)) return bl::FAM_LDS;
-    if (family_can_run_potrf(bl::FAM_BLOCKED, dt, n, stride)) return bl::FAM_BLOCKED;
+    if (family_can_run_potrf(bl::FAM_LDS, dt, n, lda, stride)) return bl::FAM_LDS;
+    if (family_can_run_potrf(bl::FAM_BLOCKED, dt, n, lda, stride)) return bl::FAM_BLOCKED;
     if (tiny) return bl::FAM_TINY;
     return bl::FAM_AUTO;
 }
 
-batchlas_status route_potrf(int requested, DT dt, int n, int64_t stride, int64_t batch,
+batchlas_status route_potrf(int requested, DT dt, int n, int64_t lda, int64_t stride, int64_t batch,
                             Geometry& g) {
     int fam = requested;
     if (fam == bl::FAM_AUTO) {
@@ -173,13 +173,13 @@ batchlas_status route_potrf(int requested, DT dt, int n, int64_t stride, int64_t
                         "(auto|tiny|lds|blocked)");
         fam = e.potrf_pin;
     }
-    if (fam == bl::FAM_AUTO) fam = auto_potrf_family(dt, n, stride);
+    if (fam == bl::FAM_AUTO) fam = auto_potrf_family(dt, n, lda, stride);
     if (fam == bl::FAM_AUTO)
         return fail(BATCHLAS_NOT_SUPPORTED, "no potrf family serves this shape");
     if (fam != bl::FAM_TINY && fam != bl::FAM_LDS && fam != bl::FAM_BLOCKED)
         return fail(BATCHLAS_INVALID_VALUE, std::string("family ") + family_name(fam) +
                                                 " is not a potrf family");
-    if (!family_can_run_potrf(fam, dt, n, stride))
+    if (!family_can_run_potrf(fam, dt, n, lda, stride))
         return fail(BATCHLAS_NOT_SUPPORTED, std::string("potrf family ") + family_name(fam) +
                                                 " cannot run " + dtype_name(dt) + " n=" +
                                                 std::to_string(n));
@@ -193,7 +193,7 @@ batchlas_status route_potrf(int requested, DT dt, int n, int64_t stride, int64_t
     return BATCHLAS_OK;
 }
 
-batchlas_status route_posv(int requested, DT dt, int n, int nrhs, int64_t strideA,
+batchlas_status route_posv(int requested, DT dt, int n, int nrhs, int64_t lda, int64_t strideA,
                            int64_t strideB, int64_t batch, Geometry& g) {
     int fam = requested;
     if (fam == bl::FAM_AUTO) {
@@ -222,7 +222,7 @@ batchlas_status route_posv(int requested, DT dt, int n, int nrhs, int64_t stride
                                                     std::to_string(n) + " nrhs=" +
                                                     std::to_string(nrhs));
         Geometry pg;
-        batchlas_status st = route_potrf(bl::FAM_AUTO, dt, n, strideA, batch, pg);
+        batchlas_status st = route_potrf(bl::FAM_AUTO, dt, n, lda, strideA, batch, pg);
         if (st != BATCHLAS_OK) return st;
         g = pg;
         g.family = bl::FAM_POSV_SPLIT;
@@ -275,7 +275,7 @@ batchlas_status do_potrf(int family, int dt_, int uplo, int64_t n, void* A, int6
     if (st != BATCHLAS_OK) return st;
     const DT dt = static_cast<DT>(dt_);
     Geometry g;
-    st = route_potrf(family, dt, int(n), strideA, batch, g);
+    st = route_potrf(family, dt, int(n), lda, strideA, batch, g);
     if (st != BATCHLAS_OK) return st;
     st = check_device();
     if (st != BATCHLAS_OK) return st;
@@ -301,7 +301,7 @@ batchlas_status do_posv(int family, int dt_, int uplo, int64_t n, int64_t nrhs, 
     if (st != BATCHLAS_OK) return st;
     const DT dt = static_cast<DT>(dt_);
     Geometry g;
-    st = route_posv(family, dt, int(n), int(nrhs), strideA, strideB, batch, g);
+    st = route_posv(family, dt, int(n), int(nrhs), lda, strideA, strideB, batch, g);
     if (st != BATCHLAS_OK) return st;
     st = check_device();
     if (st != BATCHLAS_OK) return st;
@@ -416,9 +416,9 @@ batchlas_status batchlas_route(batchlas_family family, batchlas_dtype dt, batchl
                                           nullptr, nullptr, false);
         if (st != BATCHLAS_OK) return st;
         Geometry g;
-        st = is_posv ? route_posv(family, static_cast<DT>(dt), int(n), int(nrhs), strideA,
+        st = is_posv ? route_posv(family, static_cast<DT>(dt), int(n), int(nrhs), lda, strideA,
                                   n * nrhs, batch, g)
-                     : route_potrf(family, static_cast<DT>(dt), int(n), strideA, batch, g);
+                     : route_potrf(family, static_cast<DT>(dt), int(n), lda, strideA, batch, g);
         if (st != BATCHLAS_OK) return st;
         out->family = g.family;
         out->lanes_per_matrix = g.P;

@@ -53,7 +53,7 @@ hipError_t lds_potrf(DT dt, bool upper, int n, void* A, int64_t lda, int64_t str
                      int64_t batch, int32_t* info, hipStream_t s);
 
 // --- blocked: panel kernel + MFMA trailing update
-bool blocked_supported(DT dt, int n);
+bool blocked_supported(DT dt, int n, int64_t lda);   // byte offsets of a matrix fit in 31 bits
 bool blocked_geometry(DT dt, int n, int64_t batch, Geometry& g);
 hipError_t blocked_potrf(DT dt, bool upper, int n, void* A, int64_t lda, int64_t stride,
                          int64_t batch, int32_t* info, hipStream_t s);

@@ -4,18 +4,6 @@
 
 namespace bl {
 
-int lds_max_n(DT) { return 0; }
-bool lds_geometry(DT, int, int64_t, Geometry&) { return false; }
-hipError_t lds_potrf(DT, bool, int, void*, int64_t, int64_t, int64_t, int32_t*, hipStream_t) {
-    return hipErrorNotSupported;
-}
-
-bool blocked_supported(DT, int) { return false; }
-bool blocked_geometry(DT, int, int64_t, Geometry&) { return false; }
-hipError_t blocked_potrf(DT, bool, int, void*, int64_t, int64_t, int64_t, int32_t*, hipStream_t) {
-    return hipErrorNotSupported;
-}
-
 int potrs_max_nrhs() { return 0; }
 bool potrs_supported(DT, int, int) { return false; }
 hipError_t potrs(DT, bool, int, int, const void*, int64_t, int64_t, void*, int64_t, int64_t, int64_t,

@@ -1,0 +1,119 @@
+"""GPU parity of the blocked family (panel factor + inverse, MFMA GEMM and
+triangular solve, one workgroup per matrix) against the CPU oracle.
+
+info bit-exact on every item (failures planted in the first, a middle and the
+last panel, and inside a panel); factor within 1e-4 (fp32) / 1e-11 (fp64)
+relative Frobenius error per item; the other triangle and the padding are
+bit-identical to the input.  The full-size fp64 n = 512 batch is checked on
+every info value and on a sample of factors that the oracle computes item by
+item.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as syn
+from tests._checks import RESIDUAL_BOUND, TOL, factor_residual, rel_err_triangle
+from tests._gpu import announce, check_potrf, gpu_potrf
+
+pytestmark = pytest.mark.gpu
+
+ORDERS = [1, 2, 15, 16, 17, 31, 32, 33, 47, 64, 65, 97, 128, 130, 200, 255, 256, 300, 511, 512]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    import dense_linear_algebra_potrf_amd as bl
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    bl.load_library()
+    yield
+
+
+def plant_at(a: np.ndarray, cols) -> np.ndarray:
+    """Negate A(k, k) of item b at cols[b] (None: no plant); returns the expected info."""
+    want = np.zeros(a.shape[0], np.int32)
+    for b, k in enumerate(cols):
+        if k is not None and k < a.shape[1]:
+            a[b, k, k] = -a[b, k, k]
+            want[b] = k + 1
+    return want
+
+
+@pytest.mark.parametrize("dt", ["f32", "f64"])
+@pytest.mark.parametrize("uplo", ["L", "U"])
+def test_blocked_orders(dt, uplo):
+    for n in ORDERS:
+        batch = 6 if n > 256 else 11
+        a = syn.spd_matrices(n, batch, dt, seed=40 * n + (uplo == "U"))
+        cols = [None, 0, n // 2, n - 1, 31, 32, None, 33, 100, 63, 64][:batch]
+        want = plant_at(a, cols)
+        check_potrf(a, uplo, family="blocked", expect_info=want, label="blocked-orders")
+
+
+@pytest.mark.parametrize("dt", ["f32", "f64"])
+@pytest.mark.parametrize("uplo", ["L", "U"])
+def test_blocked_poison_and_padding(dt, uplo):
+    for n in (40, 100, 300):
+        a = syn.spd_matrices(n, 5, dt, seed=n)
+        plant_at(a, [None, 3, None, n - 2, None])
+        for fill in (syn.nan_value(dt), syn.sentinel(dt)):
+            check_potrf(a, uplo, family="blocked", padded=True, fill=fill, label="blocked-poison")
+
+
+@pytest.mark.parametrize("dt", ["f64"])
+def test_blocked_packed_batch_is_independent(dt):
+    n = 300
+    one = syn.spd_matrices(n, 1, dt, seed=8)
+    solo_out, _ = gpu_potrf(syn.to_colmajor(one), "L", n, 1, n, n * n, family="blocked")
+    batch = 700
+    out, info = gpu_potrf(syn.to_colmajor(np.repeat(one, batch, axis=0)), "L", n, batch, n,
+                          n * n, family="blocked")
+    assert (info == 0).all()
+    res = out.reshape(batch, n * n)
+    assert np.array_equal(res.view(np.uint8), np.broadcast_to(solo_out.reshape(1, n * n),
+                                                              res.shape).view(np.uint8))
+
+
+@pytest.mark.parametrize("planted", [False, True])
+def test_config_fp64_n512_b1024(planted):
+    """The full workload: every info value, and the factor of a sample of items."""
+    import torch
+    import dense_linear_algebra_potrf_amd as bl
+    n, batch = 512, 1024
+    announce("config fp64 n=512 b1024", "planted" if planted else "clean")
+    a = syn.spd_matrices(n, batch, "f64", seed=1005, chunk=64)
+    want = np.zeros(batch, np.int32)
+    if planted:
+        # panels 0, 7 and 15, and a column inside a panel
+        rng = np.random.default_rng(1005)
+        for b in range(0, batch, 64):
+            k = int(rng.choice([0, 5, 224, 250, 480, 511]))
+            a[b, k, k] = -a[b, k, k]
+            want[b] = k + 1
+    t = torch.from_numpy(syn.to_colmajor(a)).cuda()
+    info = bl.potrf(t, "L", n=n, batch=batch)
+    torch.cuda.synchronize()
+    info = info.cpu().numpy()
+    assert np.array_equal(info, want)
+    out = t.cpu().numpy().reshape(batch, n * n)
+    del t
+    sample = np.array(sorted(set([0, 1, 63, 64, 65, 511, 512, 1023] +
+                                 list(np.random.default_rng(5).integers(0, batch, 8)))))
+    sub = a[sample]
+    ref = syn.to_colmajor(sub)
+    info_ref = oracle.potrf(ref, "L", n, len(sample))
+    assert np.array_equal(info_ref, want[sample])
+    got = syn.from_colmajor(out[sample].ravel(), n, n, len(sample))
+    exp = syn.from_colmajor(ref, n, n, len(sample))
+    ok = np.nonzero(info_ref == 0)[0]
+    if ok.size:
+        err = rel_err_triangle(got, exp, "L", ok)
+        assert err.max() <= TOL["f64"], f"factor error {err.max():.3e}"
+        assert factor_residual(sub, got, "L", ok).max() <= RESIDUAL_BOUND
+    # upper triangle untouched on every sampled item
+    iu = np.triu_indices(n, 1)
+    src = syn.from_colmajor(syn.to_colmajor(sub), n, n, len(sample))
+    assert np.array_equal(got[:, iu[0], iu[1]], src[:, iu[0], iu[1]])

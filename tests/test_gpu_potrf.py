@@ -66,8 +66,58 @@ def test_tiny_poison_and_padding(dt, uplo):
             check_potrf(a, uplo, family="tiny", padded=True, fill=fill, label="poison")
 
 
+# ---------------------------------------------------------------- LDS family
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("uplo", UPLOS)
+def test_lds_orders(dt, uplo):
+    """Every order from 1 to 40, then a ragged sample up to the family's top order."""
+    top = max(n for n in range(1, 200) if runnable("lds", dt, n, uplo))
+    assert top >= 64
+    orders = list(range(1, 41)) + [47, 48, 49, 63, 64, 65, 77, 95, 96, top]
+    for n in sorted(set(k for k in orders if k <= top)):
+        a = syn.spd_matrices(n, 37, dt, seed=30 * n + (uplo == "U"))
+        want = syn.plant_failures(a, seed=n, every=5)
+        check_potrf(a, uplo, family="lds", expect_info=want, label="lds-orders")
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("uplo", UPLOS)
+def test_lds_poison_and_padding(dt, uplo):
+    for n in (3, 33, 64):
+        a = syn.spd_matrices(n, 23, dt, seed=n)
+        syn.plant_failures(a, seed=n, every=4)
+        for fill in (syn.nan_value(dt), syn.sentinel(dt)):
+            check_potrf(a, uplo, family="lds", padded=True, fill=fill, label="lds-poison")
+
+
+@pytest.mark.parametrize("dt", ["f32", "c64"])
+def test_lds_packed_batch_is_independent(dt):
+    n = 50
+    one = syn.spd_matrices(n, 1, dt, seed=5)
+    solo_out, _ = gpu_potrf(syn.to_colmajor(one), "U", n, 1, n, n * n, family="lds")
+    batch = 3001
+    out, info = gpu_potrf(syn.to_colmajor(np.repeat(one, batch, axis=0)), "U", n, batch, n,
+                          n * n, family="lds")
+    assert (info == 0).all()
+    res = out.reshape(batch, n * n)
+    assert bits_equal(res, np.broadcast_to(solo_out.reshape(1, n * n), res.shape))
+
+
+@pytest.mark.parametrize("planted", [False, True])
+def test_config_cfloat_upper_n64_b16384(planted):
+    a = syn.spd_matrices(64, 16384, "c64", seed=1004)
+    want = syn.plant_failures(a, seed=1004, every=64) if planted else np.zeros(16384, np.int32)
+    check_potrf(a, "U", expect_info=want, label="config c64 U n=64 b16384")
+
+
+def test_config_fp32_n33_b16384_lds_route():
+    a = syn.spd_matrices(33, 16384, "f32", seed=1022)
+    want = syn.plant_failures(a, seed=1022, every=64)
+    check_potrf(a, "L", family="lds", expect_info=want, label="config n=33 via lds")
+
+
 # ---------------------------------------------------------------- info semantics
-@pytest.mark.parametrize("family", ["tiny"])
+@pytest.mark.parametrize("family", ["tiny", "lds"])
 @pytest.mark.parametrize("dt", DTS)
 def test_info_first_failure_nan_and_stale_pivot(family, dt):
     n = 12
