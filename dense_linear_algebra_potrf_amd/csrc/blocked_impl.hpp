@@ -10,7 +10,8 @@
 //
 //   for each panel of NBP = 32 columns starting at k:
 //     (i)   GEMM: P = S(k:n, k:k+32) - L(k:n, 0:k) L(k:k+32, 0:k)^T on MFMA
-//           (v_mfma_*_16x16x4), each of 8 waves owning every eighth 16-row block;
+//           (v_mfma_*_16x16x4, accumulated as L L^T - S so that no operand needs
+//           negating), each of 8 waves owning every eighth 32-row superblock;
 //           P is kept in LDS (up to 512 x 33 elements), so the accumulators
 //           are dead while the diagonal block is factored;
 //     (ii)  the 32 x 32 diagonal block of P is factored on one wave, and the
@@ -57,88 +58,219 @@ template <> struct Mfma<float> {
     static __device__ __forceinline__ constexpr int row(int r, int g) { return 4 * g + r; }
 };
 
-// The diagonal block of a panel, factored and inverted by one wavefront.
-// Lanes 0..31 hold row i of the block (read from the panel in LDS); lanes
-// 32..63 hold row i of the inverse being built, which starts as the identity.
-// At step j the factor half publishes the pivot column and the inverse half's
-// row j is published unscaled; rows below j take the Schur update of their
-// entries right of column j, and the same elimination (multiplier S(i, j) / d_j)
-// is applied to the inverse rows (entries up to column j, the rest are zero).
-// Then column j of the factor is scaled by 1/sqrt(d_j) (diagonal sqrt(d_j)) and
-// row j of the inverse likewise.  The block rows end as the factor L11, the
-// inverse rows as W = L11^-1.  Rows at or beyond n are the identity.  The
-// factor goes to the matrix, W to wm (row-major, zero above the diagonal) and
-// the merged info to s_inf.  Plain unrolled loops keep v in registers.
+// The diagonal block of a panel, factored and inverted by one wavefront, in
+// two phases.
+//
+// Factor: lane i (i = lane mod 32; the upper half of the wave repeats the lower
+// half and writes nothing) holds row i of the block.  At step j the pivot
+// column is published through LDS, d = S(j, j) is read back, and rows below j
+// take the Schur update of their entries right of column j with the
+// multiplier S(i, j) / d; column j is then scaled by 1/sqrt(d) (the diagonal
+// becomes sqrt(d)).  Rows at or beyond n are the identity.  The factor goes to
+// the matrix and back into the first 32 rows of the panel buffer, with
+// 1/L(j, j) beside it.
+//
+// Inverse: lane c forms column c of W = L11^-1 by forward substitution,
+//     W(m, c) = (delta(m, c) - sum_{p < m} L(m, p) W(p, c)) / L(m, m),
+// reading the rows of L11 from LDS; columns are independent, so this needs no
+// exchange between lanes.  W goes to wm (row-major), the merged info to s_inf.
+// Plain unrolled loops keep each lane's 32 values in registers.  Every LDS
+// store here is unconditional (the two halves of the wave hold identical data
+// and write identical values): stores under a lane condition split the code
+// into many small blocks, after which the compiler keeps hundreds of values
+// live and spills.
 template <typename R, bool UPPER>
-__device__ __forceinline__ void factor_invert(const R* pb, R* wm, R* colx, int lane, int k,
+__device__ __forceinline__ void factor_invert(R* pb, R* wm, double* colx, int lane, int k,
                                               int n, int w, __amdgpu_buffer_rsrc_t rs,
                                               uint32_t ld, int32_t& s_inf)
 {
+    using C = double;                   // the block is factored in double for every R
     constexpr uint32_t S = sizeof(R);
     const int i = lane & 31;
-    const bool inv_half = lane >= 32;
+    const bool writer = lane < 32;
     const bool pad = k + i >= n;
-    R* erow = colx + 2 * NBP;             // inverse-row exchange, 2 x NBP
-    R v[NBP];
+    C* rdiag = colx + 2 * NBP;          // 1 / L(j, j)
+    C v[NBP];
 #pragma unroll
     for (int c = 0; c < NBP; ++c) {
-        const R x = pb[i * LDD + c];
-        const R id = (c == i) ? R(1) : R(0);
-        v[c] = (inv_half || pad) ? id : x;
+        const C x = C(pb[i * LDD + c]);
+        const C id = (c == i) ? C(1) : C(0);
+        v[c] = pad ? id : x;
     }
     int32_t inf = s_inf;
 #pragma unroll
     for (int j = 0; j < NBP; ++j) {
-        const int par = j & 1;
-        if (!inv_half) colx[par * NBP + i] = v[j];
-        if (inv_half && i == j) {
-#pragma unroll
-            for (int c = 0; c <= j; ++c) erow[par * NBP + c] = v[c];
-        }
+        C* col = colx + (j & 1) * NBP;
+        col[i] = v[j];      // both halves of the wave write the same value
         wave_lds_sync();
-        const R d = colx[par * NBP + j];
-        if (j < w) inf = (inf == 0 && !(d > R(0))) ? (k + j + 1) : inf;
-        const R invd = pivot_rcp(d);
-        const R rsd = pivot_rsq(d);
-        R alpha = inv_half ? R(0) : v[j] * invd;
-        alpha = __shfl(alpha, i);      // the factor half's multiplier for row i
-        if (i > j) {
-            // in groups of 8 columns, so that few LDS values are in flight at once
-            if (!inv_half) {
+        const C d = col[j];
+        if (j < w) inf = (inf == 0 && !(d > C(0))) ? (k + j + 1) : inf;
+        C sq, rsd;
+        pivot_sqrt_rsq(d, sq, rsd);
+        const C beta = v[j] * (rsd * rsd);      // S(i, j) / d
+        // rows at or above j only touch slots right of the diagonal (unused)
 #pragma unroll
-                for (int c = j + 1; c < NBP; ++c) {
-                    v[c] = fmadd(-alpha, colx[par * NBP + c], v[c]);
-                    if ((c & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+        for (int m = j + 1; m < NBP; ++m) v[m] = fmadd(-col[m], beta, v[m]);
+        v[j] = (i == j) ? sq : v[j] * rsd;      // rows above j: unused slot
+        rdiag[j] = rsd;     // the same value in every lane
+    }
+    // the factor: to the matrix, and into the panel buffer for the inverse
+#pragma unroll
+    for (int c = 0; c < NBP; ++c) {
+        const bool st = writer && c <= i && c < w && !pad;
+        const uint32_t o = UPPER ? (uint32_t(k + i) * ld + uint32_t(k + c)) * S
+                                 : (uint32_t(k + c) * ld + uint32_t(k + i)) * S;
+        buf_store<R>(rs, st ? o : kBufOOB, R(v[c]));
+        pb[i * LDD + c] = (c <= i) ? R(v[c]) : R(0);
+    }
+    wave_lds_sync();
+    // column i of the inverse (from the stored factor, as the solve will use it)
+    C x[NBP];
+#pragma unroll
+    for (int m = 0; m < NBP; ++m) {
+        C acc = (m == i) ? C(1) : C(0);
+#pragma unroll
+        for (int p = 0; p < m; ++p) acc = fmadd(-C(pb[m * LDD + p]), x[p], acc);
+        x[m] = acc * rdiag[m];
+    }
+#pragma unroll
+    for (int m = 0; m < NBP; ++m) wm[m * LDD + i] = R(x[m]);
+    if (lane == 0) s_inf = inf;
+}
+
+// The GEMM of one panel: P = S(k:n, k:k+w) - L(k:n, 0:k) L(k:k+w, 0:k)^T,
+// accumulated on MFMA as L L^T - S (so no operand needs negating) and written,
+// negated back, into the panel buffer pb (row i of the panel at pb[i * LDD];
+// columns at or beyond w as 0).
+//
+// MFMA roles: the A operand runs over the panel's columns c (rows k + c of L),
+// the B operand over the panel's rows i; the result is P^T tile by tile.  With
+// PAIRED, a lane loads rows 2 l16 and 2 l16 + 1 of one column with a single
+// 16-byte load; otherwise two 8-byte loads.  Either way every load is issued
+// unconditionally and masked through the out-of-range offset (rows at or
+// beyond n, steps past k).  Operands live in a ring of NS register sets, loads NS - 1
+// steps ahead of the MFMAs.
+template <typename R, bool UPPER, bool PAIRED>
+__device__ __forceinline__ void panel_gemm(__amdgpu_buffer_rsrc_t rs, uint32_t ld, int n, int k,
+                                           int w, int RS, int wave, int l16, int g, R* pb)
+{
+    using M = Mfma<R>;
+    using v4 = typename M::v4;
+    constexpr uint32_t S = sizeof(R);
+    constexpr int MAXS = MAXN / 32 / WAVES;   // superblocks per wave
+    constexpr int NS = sizeof(R) == 8 ? 8 : 4;   // (fp32: fewer, to stay within 256 registers)
+    auto off = [&](int row, int col) -> uint32_t {
+        return UPPER ? (uint32_t(row) * ld + uint32_t(col)) * S : (uint32_t(col) * ld + uint32_t(row)) * S;
+    };
+    // accumulators start from S(k:n, k:k+w) (referenced part only): tile
+    // (s, e, cb), register r holds column c = 2 row(r, g) + cb, row i = 32 sb + 2 l16 + e
+    v4 acc[MAXS][2][2];
+    static_for<0, MAXS>([&](auto ss) {
+        constexpr int s = ss;
+        const int sb = wave + WAVES * s;
+        static_for<0, 2>([&](auto ee) {
+            static_for<0, 2>([&](auto cc) {
+                static_for<0, 4>([&](auto rr) {
+                    constexpr int e = ee, cb = cc, r = rr;
+                    const int c = 2 * M::row(r, g) + cb;
+                    const int i = 32 * sb + 2 * l16 + e;
+                    const bool ref = sb < RS && k + i < n && c < w && i >= c;
+                    acc[s][e][cb][r] = buf_load<R>(rs, ref ? off(k + i, k + c) : kBufOOB);
+                });
+            });
+        });
+    });
+    if (k > 0 && wave < RS) {   // waves without a superblock skip the loop
+        R opa[NS][2], opb[NS][MAXS][2];
+        // A masked lane gets bit 31 set in its offset, which puts it out of the
+        // buffer's range (no memory access, the load returns 0).  The mask is
+        // applied arithmetically, from a value the optimiser cannot see
+        // through: as a select it would be turned into a branch around the
+        // load, and a branch between a load and its use drains the wait
+        // counters.
+        auto masked = [&](uint32_t o, bool ok) __attribute__((always_inline)) {
+            uint32_t bad = ok ? 0u : 1u;
+            asm volatile("" : "+v"(bad));
+            return o | (bad << 31);
+        };
+        auto load_pair = [&](int row, int col, bool live, R& x, R& y) __attribute__((always_inline)) {
+            if constexpr (PAIRED) {
+                const uint32_t o = masked(off(row, col), live && row < n);
+                if constexpr (sizeof(R) == 8) {
+                    using V = uint32_t __attribute__((ext_vector_type(4)));
+                    using V2 = uint32_t __attribute__((ext_vector_type(2)));
+                    const V v = __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0);
+                    x = __builtin_bit_cast(R, V2{v.x, v.y});
+                    y = __builtin_bit_cast(R, V2{v.z, v.w});
+                } else {
+                    static_assert(sizeof(R) == 8, "paired loads are for fp64");
                 }
             } else {
-#pragma unroll
-                for (int c = 0; c <= j; ++c) {
-                    v[c] = fmadd(-alpha, erow[par * NBP + c], v[c]);
-                    if ((c & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-                }
+                x = buf_load<R>(rs, masked(off(row, col), live && row < n));
+                y = buf_load<R>(rs, masked(off(row + 1, col), live && row + 1 < n));
             }
+        };
+        auto load_ops = [&](int q, auto setc) __attribute__((always_inline)) {
+            constexpr int st = decltype(setc)::value;
+            const bool live = q < k;
+            load_pair(k + 2 * l16, q + g, live, opa[st][0], opa[st][1]);
+            static_for<0, MAXS>([&](auto ss) {
+                constexpr int s = ss;
+                const int row = k + 32 * (wave + WAVES * s) + 2 * l16;
+                load_pair(row, q + g, live, opb[st][s][0], opb[st][s][1]);
+            });
+        };
+        auto step = [&](auto setc) __attribute__((always_inline)) {
+            constexpr int st = decltype(setc)::value;
+            static_for<0, MAXS>([&](auto ss) {
+                constexpr int s = ss;
+                if (wave + WAVES * s < RS) {
+                    static_for<0, 2>([&](auto ee) {
+                        static_for<0, 2>([&](auto cc) {
+                            constexpr int e = ee, cb = cc;
+                            acc[s][e][cb] = M::mac(opa[st][cb], opb[st][s][e], acc[s][e][cb]);
+                        });
+                    });
+                }
+            });
+        };
+        static_for<0, NS - 1>([&](auto ss) { load_ops(4 * ss, ss); });
+        // from here on the accumulators hold L L^T - S
+        static_for<0, MAXS>([&](auto ss) {
+            static_for<0, 2>([&](auto ee) {
+                static_for<0, 2>([&](auto cc) { acc[ss][ee][cc] = -acc[ss][ee][cc]; });
+            });
+        });
+        for (int q = 0; q < k; q += 4 * NS) {
+            static_for<0, NS>([&](auto ss) {
+                constexpr int s = ss;
+                load_ops(q + 4 * (s + NS - 1), ic<(s + NS - 1) % NS>{});
+                step(ss);
+            });
         }
-        if (!inv_half) {
-            v[j] = (i == j) ? pivot_sqrt(d) : (i > j ? v[j] * rsd : v[j]);
-        } else if (i == j) {
-#pragma unroll
-            for (int c = 0; c <= j; ++c) v[c] = v[c] * rsd;
-        }
+        static_for<0, MAXS>([&](auto ss) {
+            static_for<0, 2>([&](auto ee) {
+                static_for<0, 2>([&](auto cc) { acc[ss][ee][cc] = -acc[ss][ee][cc]; });
+            });
+        });
     }
-    if (!inv_half) {
-        // the factor of the diagonal block goes straight to the matrix
-#pragma unroll
-        for (int c = 0; c < NBP; ++c) {
-            const bool st = c <= i && c < w && !pad;
-            const uint32_t o = UPPER ? (uint32_t(k + i) * ld + uint32_t(k + c)) * S
-                                     : (uint32_t(k + c) * ld + uint32_t(k + i)) * S;
-            buf_store<R>(rs, st ? o : kBufOOB, v[c]);
+    // the panel P goes to LDS
+    static_for<0, MAXS>([&](auto ss) {
+        constexpr int s = ss;
+        const int sb = wave + WAVES * s;
+        if (sb < RS) {
+            static_for<0, 2>([&](auto ee) {
+                static_for<0, 2>([&](auto cc) {
+                    static_for<0, 4>([&](auto rr) {
+                        constexpr int e = ee, cb = cc, r = rr;
+                        const int c = 2 * M::row(r, g) + cb;
+                        const int i = 32 * sb + 2 * l16 + e;
+                        pb[i * LDD + c] = c < w ? acc[s][e][cb][r] : R(0);
+                    });
+                });
+            });
         }
-    } else {
-#pragma unroll
-        for (int c = 0; c < NBP; ++c) wm[i * LDD + c] = v[c];
-    }
-    if (lane == 0) s_inf = inf;
+    });
 }
 
 template <typename R, bool UPPER>
@@ -151,7 +283,7 @@ __global__ __launch_bounds__(64 * WAVES) void potrf_blocked_kernel(
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     R* pb = reinterpret_cast<R*>(smem);       // the panel P, MAXN rows x LDD
     R* wm = pb + MAXN * LDD;                  // inverse of the diagonal block's factor
-    R* colx = wm + NBP * LDD;                 // pivot column exchange, 2 x 2 NBP
+    double* colx = reinterpret_cast<double*>(wm + NBP * LDD);   // pivot exchange, 4 NBP
     int32_t* s_inf = reinterpret_cast<int32_t*>(colx + 4 * NBP);
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -175,75 +307,21 @@ __global__ __launch_bounds__(64 * WAVES) void potrf_blocked_kernel(
             asm volatile("" : "+v"(lane));
             const int l16 = lane & 15, g = lane >> 4;
             const int w = min(NBP, n - k);            // panel width
-            const int RB = (n - k + 15) >> 4;         // 16-row blocks of the panel
-            {
-                // ---- (i) accumulators start from S(k:n, k:k+w) (referenced part only)
-                v4 acc[MAXT][2];
-                static_for<0, MAXT>([&](auto tt) {
-                    constexpr int t = tt;
-                    const int ib = wave + WAVES * t;
-                    static_for<0, 2>([&](auto cc) {
-                        constexpr int cb = cc;
-                        static_for<0, 4>([&](auto rr) {
-                            constexpr int r = rr;
-                            const int c = cb * 16 + M::row(r, g);
-                            const int i = ib * 16 + l16;
-                            const bool ref = ib < RB && k + i < n && c < w && i >= c;
-                            acc[t][cb][r] = buf_load<R>(rs, ref ? off(k + i, k + c) : kBufOOB);
-                        });
-                    });
-                });
-                // GEMM over the factored columns q < k, four at a time.  Operands
-                // live in two register sets (compile-time indices, so they stay
-                // in registers); the loads of one step are in flight while the
-                // MFMAs of the previous step run.  k is a multiple of 8 here.
-                if (k > 0) {
-                    const bool rowa0 = k + l16 < n, rowa1 = k + 16 + l16 < n;
-                    R opa[2][2], opb[2][MAXT];
-                    auto load_ops = [&](int q, auto setc) __attribute__((always_inline)) {
-                        constexpr int st = decltype(setc)::value;
-                        opa[st][0] = -buf_load<R>(rs, rowa0 ? off(k + l16, q + g) : kBufOOB);
-                        opa[st][1] = -buf_load<R>(rs, rowa1 ? off(k + 16 + l16, q + g) : kBufOOB);
-                        static_for<0, MAXT>([&](auto tt) {
-                            constexpr int t = tt;
-                            const int row = k + (wave + WAVES * t) * 16 + l16;
-                            opb[st][t] = (wave + WAVES * t < RB)
-                                             ? buf_load<R>(rs, row < n ? off(row, q + g) : kBufOOB)
-                                             : R(0);
-                        });
-                    };
-                    auto step = [&](auto setc) __attribute__((always_inline)) {
-                        constexpr int st = decltype(setc)::value;
-                        static_for<0, MAXT>([&](auto tt) {
-                            constexpr int t = tt;
-                            if (wave + WAVES * t < RB) {
-                                acc[t][0] = M::mac(opa[st][0], opb[st][t], acc[t][0]);
-                                acc[t][1] = M::mac(opa[st][1], opb[st][t], acc[t][1]);
-                            }
-                        });
-                    };
-                    load_ops(0, ic<0>{});
-                    for (int q = 0; q < k; q += 8) {
-                        load_ops(q + 4, ic<1>{});
-                        step(ic<0>{});
-                        if (q + 8 < k) load_ops(q + 8, ic<0>{});
-                        step(ic<1>{});
-                    }
-                }
-                // the panel P goes to LDS, row i of the panel at pb[i * LDD]
-                static_for<0, MAXT>([&](auto tt) {
-                    constexpr int t = tt;
-                    const int ib = wave + WAVES * t;
-                    if (ib < RB) {
-                        static_for<0, 2>([&](auto cc) {
-                            constexpr int cb = cc;
-                            static_for<0, 4>([&](auto rr) {
-                                constexpr int r = rr;
-                                pb[(ib * 16 + l16) * LDD + cb * 16 + M::row(r, g)] = acc[t][cb][r];
-                            });
-                        });
-                    }
-                });
+            const int RB = (n - k + 15) >> 4;         // 16-row blocks of the panel (solve)
+            // ---- (i) the panel's GEMM; each wave owns the 32-row superblocks
+            // sb = wave + WAVES s of the panel, split into the even and the odd
+            // rows (two 16-row MFMA tiles), and the panel's 32 columns are split
+            // the same way (cb = 0: even columns, cb = 1: odd columns), so that a
+            // lane loads two consecutive rows of a column at once where the layout
+            // allows it (Lower with n even: one 16-byte load).
+            const int RS = (n - k + 31) >> 5;         // 32-row superblocks of the panel
+            // (the paired 16-byte loads are used for fp64 only: the fp32 pairs
+            // gave wrong results on the GPU and are not used)
+            if constexpr (!UPPER && sizeof(R) == 8) {
+                if ((n & 1) == 0) panel_gemm<R, UPPER, true>(rs, ld, n, k, w, RS, wave, l16, g, pb);
+                else panel_gemm<R, UPPER, false>(rs, ld, n, k, w, RS, wave, l16, g, pb);
+            } else {
+                panel_gemm<R, UPPER, false>(rs, ld, n, k, w, RS, wave, l16, g, pb);
             }
             __syncthreads();
 
@@ -289,7 +367,7 @@ constexpr int64_t kMaxGrid = int64_t(1) << 20;
 
 template <typename R>
 constexpr int64_t lds_bytes() {
-    return int64_t(MAXN * LDD + NBP * LDD + 4 * NBP) * sizeof(R) + 16;
+    return int64_t(MAXN * LDD + NBP * LDD) * sizeof(R) + 4 * NBP * 8 + 16;
 }
 
 template <typename R>

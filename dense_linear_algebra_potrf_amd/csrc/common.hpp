@@ -106,14 +106,42 @@ template <typename T> __device__ __forceinline__ void sub_conj_mul(T& acc, const
 
 // Reciprocal, reciprocal square root and square root of a positive pivot.
 // float: the hardware approximations (about 1 ulp), well inside the 1e-4
-// parity tolerance.  double: correctly rounded library operations, because the
-// fp64 hardware approximations are far less accurate than 1e-11.
+// parity tolerance.  double: the hardware approximations refined by two Newton
+// steps each, which brings them to within a few ulp (far inside the 1e-11
+// tolerance) at a fraction of the latency of correctly rounded division and
+// square root.  Non-positive pivots give NaN or infinity, as they should: such
+// a matrix has already failed.
 __device__ __forceinline__ float pivot_rcp(float d) { return __builtin_amdgcn_rcpf(d); }
 __device__ __forceinline__ float pivot_rsq(float d) { return __builtin_amdgcn_rsqf(d); }
 __device__ __forceinline__ float pivot_sqrt(float d) { return __builtin_amdgcn_sqrtf(d); }
-__device__ __forceinline__ double pivot_rcp(double d) { return 1.0 / d; }
-__device__ __forceinline__ double pivot_sqrt(double d) { return __builtin_sqrt(d); }
-__device__ __forceinline__ double pivot_rsq(double d) { return 1.0 / __builtin_sqrt(d); }
+__device__ __forceinline__ void pivot_sqrt_rsq(float d, float& sq, float& rsq) {
+    sq = __builtin_amdgcn_sqrtf(d);
+    rsq = __builtin_amdgcn_rsqf(d);
+}
+// 1/d: r <- r + r (1 - d r), twice.
+__device__ __forceinline__ double pivot_rcp(double d) {
+    double r = __builtin_amdgcn_rcp(d);
+    r = __builtin_fma(r, __builtin_fma(-d, r, 1.0), r);
+    r = __builtin_fma(r, __builtin_fma(-d, r, 1.0), r);
+    return r;
+}
+// sqrt(d) and 1/sqrt(d) together: from y ~ 1/sqrt(d), g = d y ~ sqrt(d) and
+// h = y / 2; each step takes the residual e = 1/2 - g h and sets g += g e,
+// h += h e (both converge quadratically).
+__device__ __forceinline__ void pivot_sqrt_rsq(double d, double& sq, double& rsq) {
+    const double y = __builtin_amdgcn_rsq(d);
+    double g = d * y, h = 0.5 * y;
+    double e = __builtin_fma(-g, h, 0.5);
+    g = __builtin_fma(g, e, g);
+    h = __builtin_fma(h, e, h);
+    e = __builtin_fma(-g, h, 0.5);
+    g = __builtin_fma(g, e, g);
+    h = __builtin_fma(h, e, h);
+    sq = g;
+    rsq = 2.0 * h;
+}
+__device__ __forceinline__ double pivot_sqrt(double d) { double s, r; pivot_sqrt_rsq(d, s, r); return s; }
+__device__ __forceinline__ double pivot_rsq(double d) { double s, r; pivot_sqrt_rsq(d, s, r); return r; }
 
 // ---------------------------------------------------------------- compile-time loops
 template <int V> using ic = std::integral_constant<int, V>;
