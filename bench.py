@@ -117,17 +117,21 @@ def bench_config(name: str, steps: int, warmup: int) -> dict:
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     flush.fill_(7)
     del flush
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    # Two events bracket the whole timed region on the launch stream: an event
+    # between launches would itself open a gap of several microseconds.  Every
+    # family is a single launch per call, so the region's time over K is the
+    # average duration of the dominant kernel.
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for k in range(steps):
-        ev0[k].record(stream)
         launch(warmup + k)
-        ev1[k].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [ev0[k].elapsed_time(ev1[k]) for k in range(steps)]
+    kern_ms = [ev0.elapsed_time(ev1) / steps]
     # correctness guard on the last step: info must be as planted
     info_h = info.cpu().numpy()
     if cfg.get("plant"):
@@ -138,7 +142,7 @@ def bench_config(name: str, steps: int, warmup: int) -> dict:
         assert (info_h == 0).all(), f"{name}: unexpected info"
 
     ms_step = wall * 1e3 / steps
-    ms_kernel = sum(kern_ms) / steps
+    ms_kernel = kern_ms[0]
     if cfg["op"] == "potrf":
         byts = metrics.potrf_bytes(n, batch, dt, uplo)
         flops = metrics.potrf_flops(n, dt) * batch
@@ -188,18 +192,20 @@ def attach_traffic(name: str, res: dict) -> None:
     res["roofline"]["traffic"] = rec.get("traffic_bytes")
 
 
-def cpu_baseline(name: str, budget_s: float = 1.5) -> dict:
-    """The oracle on the host cores, on a bounded sample of the same workload."""
+def cpu_baseline(name: str, cpu_seconds: float = 16.0) -> dict:
+    """The oracle on the host cores, on a bounded sample of the same workload
+    (about cpu_seconds of CPU work: wall time times threads)."""
     import numpy as np
     import oracle
     cfg = CONFIGS[name]
     threads = max(1, min(16, os.cpu_count() or 1))
+    budget_s = cpu_seconds / threads
     n, dt = cfg["n"], cfg["dt"]
     per = max(1, min(cfg["batch"], int(2e8 // max(1, n ** 3))))   # first sample size
     sample = dict(cfg, batch=per)
     abuf, bbuf = make_input(sample)
     done, t = 0, 0.0
-    while t < budget_s and done < 64 * cfg["batch"]:
+    while t < budget_s:
         a = abuf.copy()
         b = bbuf.copy() if bbuf is not None else None
         t0 = time.perf_counter()
