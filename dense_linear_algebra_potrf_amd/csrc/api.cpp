@@ -162,8 +162,8 @@ int auto_potrf_family(DT dt, int n, int64_t lda, int64_t stride) {
     return bl::FAM_AUTO;
 }
 
-batchlas_status route_potrf(int requested, DT dt, int n, int64_t lda, int64_t stride, int64_t batch,
-                            Geometry& g) {
+batchlas_status route_potrf(int requested, DT dt, bool upper, int n, int64_t lda, int64_t stride,
+                            int64_t batch, Geometry& g) {
     int fam = requested;
     if (fam == bl::FAM_AUTO) {
         const EnvSnapshot& e = env();
@@ -185,7 +185,7 @@ batchlas_status route_potrf(int requested, DT dt, int n, int64_t lda, int64_t st
                                                 std::to_string(n));
     bool ok = false;
     switch (fam) {
-    case bl::FAM_TINY: ok = bl::tiny_geometry(dt, n, batch, g); break;
+    case bl::FAM_TINY: ok = bl::tiny_geometry(dt, upper, n, lda, stride, batch, g); break;
     case bl::FAM_LDS: ok = bl::lds_geometry(dt, n, batch, g); break;
     case bl::FAM_BLOCKED: ok = bl::blocked_geometry(dt, n, batch, g); break;
     }
@@ -193,8 +193,8 @@ batchlas_status route_potrf(int requested, DT dt, int n, int64_t lda, int64_t st
     return BATCHLAS_OK;
 }
 
-batchlas_status route_posv(int requested, DT dt, int n, int nrhs, int64_t lda, int64_t strideA,
-                           int64_t strideB, int64_t batch, Geometry& g) {
+batchlas_status route_posv(int requested, DT dt, bool upper, int n, int nrhs, int64_t lda,
+                           int64_t strideA, int64_t strideB, int64_t batch, Geometry& g) {
     int fam = requested;
     if (fam == bl::FAM_AUTO) {
         const EnvSnapshot& e = env();
@@ -211,7 +211,7 @@ batchlas_status route_posv(int requested, DT dt, int n, int nrhs, int64_t lda, i
             return fail(BATCHLAS_NOT_SUPPORTED, "posv_tiny cannot run " + std::string(dtype_name(dt)) +
                                                     " n=" + std::to_string(n) + " nrhs=" +
                                                     std::to_string(nrhs));
-        if (!bl::posv_tiny_geometry(dt, n, nrhs, batch, g))
+        if (!bl::posv_tiny_geometry(dt, upper, n, nrhs, lda, strideA, batch, g))
             return fail(BATCHLAS_INTERNAL, "geometry unavailable for posv_tiny");
         return BATCHLAS_OK;
     }
@@ -222,7 +222,7 @@ batchlas_status route_posv(int requested, DT dt, int n, int nrhs, int64_t lda, i
                                                     std::to_string(n) + " nrhs=" +
                                                     std::to_string(nrhs));
         Geometry pg;
-        batchlas_status st = route_potrf(bl::FAM_AUTO, dt, n, lda, strideA, batch, pg);
+        batchlas_status st = route_potrf(bl::FAM_AUTO, dt, upper, n, lda, strideA, batch, pg);
         if (st != BATCHLAS_OK) return st;
         g = pg;
         g.family = bl::FAM_POSV_SPLIT;
@@ -275,7 +275,7 @@ batchlas_status do_potrf(int family, int dt_, int uplo, int64_t n, void* A, int6
     if (st != BATCHLAS_OK) return st;
     const DT dt = static_cast<DT>(dt_);
     Geometry g;
-    st = route_potrf(family, dt, int(n), lda, strideA, batch, g);
+    st = route_potrf(family, dt, uplo == BATCHLAS_UPPER, int(n), lda, strideA, batch, g);
     if (st != BATCHLAS_OK) return st;
     st = check_device();
     if (st != BATCHLAS_OK) return st;
@@ -301,7 +301,8 @@ batchlas_status do_posv(int family, int dt_, int uplo, int64_t n, int64_t nrhs, 
     if (st != BATCHLAS_OK) return st;
     const DT dt = static_cast<DT>(dt_);
     Geometry g;
-    st = route_posv(family, dt, int(n), int(nrhs), lda, strideA, strideB, batch, g);
+    st = route_posv(family, dt, uplo == BATCHLAS_UPPER, int(n), int(nrhs), lda, strideA, strideB,
+                    batch, g);
     if (st != BATCHLAS_OK) return st;
     st = check_device();
     if (st != BATCHLAS_OK) return st;
@@ -416,9 +417,11 @@ batchlas_status batchlas_route(batchlas_family family, batchlas_dtype dt, batchl
                                           nullptr, nullptr, false);
         if (st != BATCHLAS_OK) return st;
         Geometry g;
-        st = is_posv ? route_posv(family, static_cast<DT>(dt), int(n), int(nrhs), lda, strideA,
-                                  n * nrhs, batch, g)
-                     : route_potrf(family, static_cast<DT>(dt), int(n), lda, strideA, batch, g);
+        const bool upper = uplo == BATCHLAS_UPPER;
+        st = is_posv ? route_posv(family, static_cast<DT>(dt), upper, int(n), int(nrhs), lda,
+                                  strideA, n * nrhs, batch, g)
+                     : route_potrf(family, static_cast<DT>(dt), upper, int(n), lda, strideA,
+                                   batch, g);
         if (st != BATCHLAS_OK) return st;
         out->family = g.family;
         out->lanes_per_matrix = g.P;

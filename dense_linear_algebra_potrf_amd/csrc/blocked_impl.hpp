@@ -24,7 +24,11 @@
 //     then the panel is written to the matrix, where the next panels read it.
 //
 // S = A for Lower, S(i, c) = conj(A(c, i)) for Upper; for the real types the
-// Upper form only swaps the address of each element.  Only the referenced
+// Upper form only swaps the address of each element.  The complex types run
+// the same schedule with each complex product split into four real MFMAs on
+// separate real and imaginary accumulators (the pages' complex trailing update
+// is a ConjTrans GEMM); cdouble is limited to order 256, where its panel
+// buffer still fits in LDS.  Only the referenced
 // triangle is read or written; rows beyond n load as zero and are never
 // stored.  Failure handling follows the pages' info contract: the first
 // failing pivot column is kept; later work runs on with NaN.
@@ -37,9 +41,25 @@ namespace blocked_detail {
 
 constexpr int NBP = 32;          // panel width
 constexpr int WAVES = 8;         // wavefronts per workgroup
-constexpr int MAXN = 512;        // largest order served
-constexpr int MAXT = MAXN / 16 / WAVES;   // 16-row blocks per wave
 constexpr int LDD = NBP + 1;     // padded row length of the LDS blocks
+
+// Largest order served (the panel buffer, MAXN x LDD elements, lives in LDS),
+// 32-row superblocks per wave in the GEMM and 16-row blocks per wave in the
+// solve.
+template <typename T> struct Shape {
+    static constexpr int MAXN = sizeof(T) == 16 ? 256 : 512;
+    static constexpr int MAXS = MAXN / 32 / WAVES;
+    static constexpr int MAXT = MAXN / 16 / WAVES;
+};
+// The diagonal block is factored in double for the real types and in the
+// element type itself for the complex ones.
+template <typename T> struct FactorType {
+    using type = typename std::conditional<Traits<T>::cplx, T, double>::type;
+};
+template <typename To, typename From> __device__ __forceinline__ To cvt(const From& x) {
+    if constexpr (Traits<To>::cplx) return x;
+    else return To(x);
+}
 
 template <typename R> struct Mfma;
 template <> struct Mfma<double> {
@@ -58,8 +78,20 @@ template <> struct Mfma<float> {
     static __device__ __forceinline__ constexpr int row(int r, int g) { return 4 * g + r; }
 };
 
-// The diagonal block of a panel, factored and inverted by one wavefront, in
-// two phases.
+// Complex multiply-accumulate on split planes: (cr, ci) += conj(a) b when CONJ,
+// else a b, as four real MFMAs.
+template <bool CONJ, typename R, typename V>
+__device__ __forceinline__ void cmac(R ar, R ai, R br, R bi, V& cr, V& ci) {
+    using M = Mfma<R>;
+    const R nai = -ai;
+    cr = M::mac(ar, br, cr);
+    cr = M::mac(CONJ ? ai : nai, bi, cr);
+    ci = M::mac(ar, bi, ci);
+    ci = M::mac(CONJ ? nai : ai, br, ci);
+}
+
+// The diagonal block of a panel (real types), factored in double and inverted
+// by one wavefront, in two phases.
 //
 // Factor: lane i (i = lane mod 32; the upper half of the wave repeats the lower
 // half and writes nothing) holds row i of the block.  At step j the pivot
@@ -79,23 +111,24 @@ template <> struct Mfma<float> {
 // and write identical values): stores under a lane condition split the code
 // into many small blocks, after which the compiler keeps hundreds of values
 // live and spills.
-template <typename R, bool UPPER>
-__device__ __forceinline__ void factor_invert(R* pb, R* wm, double* colx, int lane, int k,
-                                              int n, int w, __amdgpu_buffer_rsrc_t rs,
-                                              uint32_t ld, int32_t& s_inf)
+template <typename T, bool UPPER>
+__device__ __forceinline__ void factor_invert(T* pb, T* wm, typename FactorType<T>::type* colx,
+                                              typename Traits<typename FactorType<T>::type>::R* rdiag,
+                                              int lane, int k, int n, int w,
+                                              __amdgpu_buffer_rsrc_t rs, uint32_t ld, int32_t& s_inf)
 {
-    using C = double;                   // the block is factored in double for every R
-    constexpr uint32_t S = sizeof(R);
+    using C = typename FactorType<T>::type;
+    using Rc = typename Traits<C>::R;
+    constexpr uint32_t S = sizeof(T);
     const int i = lane & 31;
     const bool writer = lane < 32;
     const bool pad = k + i >= n;
-    C* rdiag = colx + 2 * NBP;          // 1 / L(j, j)
     C v[NBP];
 #pragma unroll
     for (int c = 0; c < NBP; ++c) {
-        const C x = C(pb[i * LDD + c]);
-        const C id = (c == i) ? C(1) : C(0);
-        v[c] = pad ? id : x;
+        const C x = cvt<C>(pb[i * LDD + c]);
+        const C id = select(c == i, one<C>(), zero<C>());
+        v[c] = select(pad, id, x);
     }
     int32_t inf = s_inf;
 #pragma unroll
@@ -103,38 +136,100 @@ __device__ __forceinline__ void factor_invert(R* pb, R* wm, double* colx, int la
         C* col = colx + (j & 1) * NBP;
         col[i] = v[j];      // both halves of the wave write the same value
         wave_lds_sync();
-        const C d = col[j];
-        if (j < w) inf = (inf == 0 && !(d > C(0))) ? (k + j + 1) : inf;
-        C sq, rsd;
+        const Rc d = re(col[j]);
+        if (j < w) inf = (inf == 0 && !(d > Rc(0))) ? (k + j + 1) : inf;
+        Rc sq, rsd;
         pivot_sqrt_rsq(d, sq, rsd);
-        const C beta = v[j] * (rsd * rsd);      // S(i, j) / d
+        const C beta = scale(v[j], rsd * rsd);      // S(i, j) / d
         // rows at or above j only touch slots right of the diagonal (unused)
 #pragma unroll
-        for (int m = j + 1; m < NBP; ++m) v[m] = fmadd(-col[m], beta, v[m]);
-        v[j] = (i == j) ? sq : v[j] * rsd;      // rows above j: unused slot
+        for (int m = j + 1; m < NBP; ++m) sub_mul_conj(v[m], beta, col[m]);
+        v[j] = select(i == j, diag_value<C>(sq, UPPER), scale(v[j], rsd));   // rows above j: unused slot
         rdiag[j] = rsd;     // the same value in every lane
     }
-    // the factor: to the matrix, and into the panel buffer for the inverse
+    // the factor: to the matrix (conjugated for Upper), and into the panel
+    // buffer for the inverse
 #pragma unroll
     for (int c = 0; c < NBP; ++c) {
         const bool st = writer && c <= i && c < w && !pad;
         const uint32_t o = UPPER ? (uint32_t(k + i) * ld + uint32_t(k + c)) * S
                                  : (uint32_t(k + c) * ld + uint32_t(k + i)) * S;
-        buf_store<R>(rs, st ? o : kBufOOB, R(v[c]));
-        pb[i * LDD + c] = (c <= i) ? R(v[c]) : R(0);
+        buf_store<T>(rs, st ? o : kBufOOB, cvt<T>(UPPER ? conj(v[c]) : v[c]));
+        pb[i * LDD + c] = (c <= i) ? cvt<T>(v[c]) : zero<T>();
     }
     wave_lds_sync();
-    // column i of the inverse (from the stored factor, as the solve will use it)
+    // column i of the inverse (from the stored factor, as the solve will use
+    // it); wm keeps conj(W) so that the solve is a plain product
     C x[NBP];
 #pragma unroll
     for (int m = 0; m < NBP; ++m) {
-        C acc = (m == i) ? C(1) : C(0);
+        C acc = select(m == i, one<C>(), zero<C>());
 #pragma unroll
-        for (int p = 0; p < m; ++p) acc = fmadd(-C(pb[m * LDD + p]), x[p], acc);
-        x[m] = acc * rdiag[m];
+        for (int p = 0; p < m; ++p) sub_mul(acc, cvt<C>(pb[m * LDD + p]), x[p]);
+        x[m] = scale(acc, rdiag[m]);
     }
 #pragma unroll
-    for (int m = 0; m < NBP; ++m) wm[m * LDD + i] = R(x[m]);
+    for (int m = 0; m < NBP; ++m) wm[m * LDD + i] = cvt<T>(conj(x[m]));
+    if (lane == 0) s_inf = inf;
+}
+
+// Complex types: the same factorisation and inverse worked in place in LDS
+// (row i of the block at pb[i * LDD], lane i owning row i, the inverse built
+// column by column in wm), so that no lane holds a whole row: with the row and
+// the column of the inverse in registers the complex kernels spill.  The
+// column of step j is read by every lane before its owners rescale it (LDS
+// instructions of one wave complete in order).
+template <typename T, bool UPPER>
+__device__ __forceinline__ void factor_invert_inplace(T* pb, T* wm, typename Traits<T>::R* rdiag,
+                                                      int lane, int k, int n, int w,
+                                                      __amdgpu_buffer_rsrc_t rs, uint32_t ld,
+                                                      int32_t& s_inf)
+{
+    using R = typename Traits<T>::R;
+    constexpr uint32_t S = sizeof(T);
+    const int i = lane & 31;
+    const bool writer = lane < 32;
+    const bool pad = k + i >= n;
+    T* row = pb + i * LDD;
+#pragma unroll 1
+    for (int c = 0; c < NBP; ++c) row[c] = select(pad, select(c == i, one<T>(), zero<T>()), row[c]);
+    wave_lds_sync();
+    int32_t inf = s_inf;
+#pragma unroll 1
+    for (int j = 0; j < NBP; ++j) {
+        const R d = re(pb[j * LDD + j]);
+        if (j < w) inf = (inf == 0 && !(d > R(0))) ? (k + j + 1) : inf;
+        R sq, rsd;
+        pivot_sqrt_rsq(d, sq, rsd);
+        const T lij = row[j];
+        const T beta = scale(lij, rsd * rsd);       // S(i, j) / d
+        // rows at or above j only touch slots right of the diagonal (unused)
+#pragma unroll 2
+        for (int m = j + 1; m < NBP; ++m) {
+            T v = row[m];
+            sub_mul_conj(v, beta, pb[m * LDD + j]);
+            row[m] = v;
+        }
+        wave_lds_sync();
+        row[j] = select(i == j, diag_value<T>(sq, UPPER), select(i > j, scale(lij, rsd), lij));
+        rdiag[j] = rsd;
+        wave_lds_sync();
+    }
+#pragma unroll 1
+    for (int c = 0; c < NBP; ++c) {
+        const bool st = writer && c <= i && c < w && !pad;
+        const uint32_t o = UPPER ? (uint32_t(k + i) * ld + uint32_t(k + c)) * S
+                                 : (uint32_t(k + c) * ld + uint32_t(k + i)) * S;
+        buf_store<T>(rs, st ? o : kBufOOB, UPPER ? conj(row[c]) : row[c]);
+    }
+    // column i of conj(W), W = L11^-1, by forward substitution
+#pragma unroll 1
+    for (int m = 0; m < NBP; ++m) {
+        T acc = select(m == i, one<T>(), zero<T>());
+#pragma unroll 2
+        for (int p = 0; p < m; ++p) sub_mul(acc, pb[m * LDD + p], conj(wm[p * LDD + i]));
+        wm[m * LDD + i] = conj(scale(acc, rdiag[m]));
+    }
     if (lane == 0) s_inf = inf;
 }
 
@@ -150,21 +245,27 @@ __device__ __forceinline__ void factor_invert(R* pb, R* wm, double* colx, int la
 // unconditionally and masked through the out-of-range offset (rows at or
 // beyond n, steps past k).  Operands live in a ring of NS register sets, loads NS - 1
 // steps ahead of the MFMAs.
-template <typename R, bool UPPER, bool PAIRED>
+template <typename T, bool UPPER, bool PAIRED>
 __device__ __forceinline__ void panel_gemm(__amdgpu_buffer_rsrc_t rs, uint32_t ld, int n, int k,
-                                           int w, int RS, int wave, int l16, int g, R* pb)
+                                           int w, int RS, int wave, int l16, int g, T* pb)
 {
+    using R = typename Traits<T>::R;
+    constexpr bool CPLX = Traits<T>::cplx;
     using M = Mfma<R>;
     using v4 = typename M::v4;
-    constexpr uint32_t S = sizeof(R);
-    constexpr int MAXS = MAXN / 32 / WAVES;   // superblocks per wave
-    constexpr int NS = sizeof(R) == 8 ? 8 : 4;   // (fp32: fewer, to stay within 256 registers)
+    constexpr uint32_t S = sizeof(T);
+    constexpr int MAXS = Shape<T>::MAXS;   // superblocks per wave
+    // ring depth (fp32 and the complex types: fewer, to stay within 256 registers)
+    constexpr int NS = (!CPLX && sizeof(R) == 8) ? 8 : 4;
     auto off = [&](int row, int col) -> uint32_t {
         return UPPER ? (uint32_t(row) * ld + uint32_t(col)) * S : (uint32_t(col) * ld + uint32_t(row)) * S;
     };
     // accumulators start from S(k:n, k:k+w) (referenced part only): tile
-    // (s, e, cb), register r holds column c = 2 row(r, g) + cb, row i = 32 sb + 2 l16 + e
-    v4 acc[MAXS][2][2];
+    // (s, e, cb), register r holds column c = 2 row(r, g) + cb, row i = 32 sb + 2 l16 + e.
+    // The complex types keep the imaginary parts in aci.  For Upper the
+    // complex arithmetic runs on the stored values, conj(S) and conj(L), which
+    // gives conj(P); the conjugate is taken when P is written out.
+    v4 acc[MAXS][2][2], aci[MAXS][2][2];
     static_for<0, MAXS>([&](auto ss) {
         constexpr int s = ss;
         const int sb = wave + WAVES * s;
@@ -175,13 +276,25 @@ __device__ __forceinline__ void panel_gemm(__amdgpu_buffer_rsrc_t rs, uint32_t l
                     const int c = 2 * M::row(r, g) + cb;
                     const int i = 32 * sb + 2 * l16 + e;
                     const bool ref = sb < RS && k + i < n && c < w && i >= c;
-                    acc[s][e][cb][r] = buf_load<R>(rs, ref ? off(k + i, k + c) : kBufOOB);
+                    const T x = buf_load<T>(rs, ref ? off(k + i, k + c) : kBufOOB);
+                    acc[s][e][cb][r] = re(x);
+                    if constexpr (CPLX) aci[s][e][cb][r] = x.im;
                 });
             });
         });
     });
+    auto negate_all = [&]() __attribute__((always_inline)) {
+        static_for<0, MAXS>([&](auto ss) {
+            static_for<0, 2>([&](auto ee) {
+                static_for<0, 2>([&](auto cc) {
+                    acc[ss][ee][cc] = -acc[ss][ee][cc];
+                    if constexpr (CPLX) aci[ss][ee][cc] = -aci[ss][ee][cc];
+                });
+            });
+        });
+    };
     if (k > 0 && wave < RS) {   // waves without a superblock skip the loop
-        R opa[NS][2], opb[NS][MAXS][2];
+        T opa[NS][2], opb[NS][MAXS][2];
         // A masked lane gets bit 31 set in its offset, which puts it out of the
         // buffer's range (no memory access, the load returns 0).  The mask is
         // applied arithmetically, from a value the optimiser cannot see
@@ -193,21 +306,18 @@ __device__ __forceinline__ void panel_gemm(__amdgpu_buffer_rsrc_t rs, uint32_t l
             asm volatile("" : "+v"(bad));
             return o | (bad << 31);
         };
-        auto load_pair = [&](int row, int col, bool live, R& x, R& y) __attribute__((always_inline)) {
+        auto load_pair = [&](int row, int col, bool live, T& x, T& y) __attribute__((always_inline)) {
             if constexpr (PAIRED) {
+                static_assert(!CPLX && sizeof(R) == 8, "paired loads are for fp64");
                 const uint32_t o = masked(off(row, col), live && row < n);
-                if constexpr (sizeof(R) == 8) {
-                    using V = uint32_t __attribute__((ext_vector_type(4)));
-                    using V2 = uint32_t __attribute__((ext_vector_type(2)));
-                    const V v = __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0);
-                    x = __builtin_bit_cast(R, V2{v.x, v.y});
-                    y = __builtin_bit_cast(R, V2{v.z, v.w});
-                } else {
-                    static_assert(sizeof(R) == 8, "paired loads are for fp64");
-                }
+                using V = uint32_t __attribute__((ext_vector_type(4)));
+                using V2 = uint32_t __attribute__((ext_vector_type(2)));
+                const V v = __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0);
+                x = __builtin_bit_cast(T, V2{v.x, v.y});
+                y = __builtin_bit_cast(T, V2{v.z, v.w});
             } else {
-                x = buf_load<R>(rs, masked(off(row, col), live && row < n));
-                y = buf_load<R>(rs, masked(off(row + 1, col), live && row + 1 < n));
+                x = buf_load<T>(rs, masked(off(row, col), live && row < n));
+                y = buf_load<T>(rs, masked(off(row + 1, col), live && row + 1 < n));
             }
         };
         auto load_ops = [&](int q, auto setc) __attribute__((always_inline)) {
@@ -228,19 +338,20 @@ __device__ __forceinline__ void panel_gemm(__amdgpu_buffer_rsrc_t rs, uint32_t l
                     static_for<0, 2>([&](auto ee) {
                         static_for<0, 2>([&](auto cc) {
                             constexpr int e = ee, cb = cc;
-                            acc[s][e][cb] = M::mac(opa[st][cb], opb[st][s][e], acc[s][e][cb]);
+                            const T& a = opa[st][cb];
+                            const T& bv = opb[st][s][e];
+                            if constexpr (CPLX)
+                                cmac<true>(a.re, a.im, bv.re, bv.im, acc[s][e][cb], aci[s][e][cb]);
+                            else
+                                acc[s][e][cb] = M::mac(a, bv, acc[s][e][cb]);
                         });
                     });
                 }
             });
         };
         static_for<0, NS - 1>([&](auto ss) { load_ops(4 * ss, ss); });
-        // from here on the accumulators hold L L^T - S
-        static_for<0, MAXS>([&](auto ss) {
-            static_for<0, 2>([&](auto ee) {
-                static_for<0, 2>([&](auto cc) { acc[ss][ee][cc] = -acc[ss][ee][cc]; });
-            });
-        });
+        // from here on the accumulators hold L L^H - S
+        negate_all();
         for (int q = 0; q < k; q += 4 * NS) {
             static_for<0, NS>([&](auto ss) {
                 constexpr int s = ss;
@@ -248,11 +359,7 @@ __device__ __forceinline__ void panel_gemm(__amdgpu_buffer_rsrc_t rs, uint32_t l
                 step(ss);
             });
         }
-        static_for<0, MAXS>([&](auto ss) {
-            static_for<0, 2>([&](auto ee) {
-                static_for<0, 2>([&](auto cc) { acc[ss][ee][cc] = -acc[ss][ee][cc]; });
-            });
-        });
+        negate_all();
     }
     // the panel P goes to LDS
     static_for<0, MAXS>([&](auto ss) {
@@ -265,7 +372,10 @@ __device__ __forceinline__ void panel_gemm(__amdgpu_buffer_rsrc_t rs, uint32_t l
                         constexpr int e = ee, cb = cc, r = rr;
                         const int c = 2 * M::row(r, g) + cb;
                         const int i = 32 * sb + 2 * l16 + e;
-                        pb[i * LDD + c] = c < w ? acc[s][e][cb][r] : R(0);
+                        T val;
+                        if constexpr (CPLX) val = T{acc[s][e][cb][r], UPPER ? -aci[s][e][cb][r] : aci[s][e][cb][r]};
+                        else val = acc[s][e][cb][r];
+                        pb[i * LDD + c] = c < w ? val : zero<T>();
                     });
                 });
             });
@@ -273,21 +383,27 @@ __device__ __forceinline__ void panel_gemm(__amdgpu_buffer_rsrc_t rs, uint32_t l
     });
 }
 
-template <typename R, bool UPPER>
+template <typename T, bool UPPER>
 __global__ __launch_bounds__(64 * WAVES) void potrf_blocked_kernel(
-    R* __restrict__ A, int n, int64_t lda, int64_t stride, int64_t batch,
+    T* __restrict__ A, int n, int64_t lda, int64_t stride, int64_t batch,
     int32_t* __restrict__ info)
 {
+    using R = typename Traits<T>::R;
+    using C = typename FactorType<T>::type;
+    using Rc = typename Traits<C>::R;
+    constexpr bool CPLX = Traits<T>::cplx;
     using M = Mfma<R>;
     using v4 = typename M::v4;
+    constexpr int MAXN = Shape<T>::MAXN, MAXT = Shape<T>::MAXT;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    R* pb = reinterpret_cast<R*>(smem);       // the panel P, MAXN rows x LDD
-    R* wm = pb + MAXN * LDD;                  // inverse of the diagonal block's factor
-    double* colx = reinterpret_cast<double*>(wm + NBP * LDD);   // pivot exchange, 4 NBP
-    int32_t* s_inf = reinterpret_cast<int32_t*>(colx + 4 * NBP);
+    T* pb = reinterpret_cast<T*>(smem);       // the panel P, MAXN rows x LDD
+    T* wm = pb + MAXN * LDD;                  // conj of the inverse of the diagonal block's factor
+    C* colx = reinterpret_cast<C*>(wm + NBP * LDD);   // pivot exchange, 2 NBP
+    Rc* rdiag = reinterpret_cast<Rc*>(colx + 2 * NBP);   // 1 / L(j, j), NBP
+    int32_t* s_inf = reinterpret_cast<int32_t*>(rdiag + NBP);
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    constexpr uint32_t S = sizeof(R);
+    constexpr uint32_t S = sizeof(T);
     const uint32_t ld = uint32_t(lda);
     // byte offset of S(row, col) inside the matrix (the host guarantees < 2^31)
     auto off = [&](int row, int col) -> uint32_t {
@@ -317,20 +433,25 @@ __global__ __launch_bounds__(64 * WAVES) void potrf_blocked_kernel(
             const int RS = (n - k + 31) >> 5;         // 32-row superblocks of the panel
             // (the paired 16-byte loads are used for fp64 only: the fp32 pairs
             // gave wrong results on the GPU and are not used)
-            if constexpr (!UPPER && sizeof(R) == 8) {
-                if ((n & 1) == 0) panel_gemm<R, UPPER, true>(rs, ld, n, k, w, RS, wave, l16, g, pb);
-                else panel_gemm<R, UPPER, false>(rs, ld, n, k, w, RS, wave, l16, g, pb);
+            if constexpr (!UPPER && !CPLX && sizeof(R) == 8) {
+                if ((n & 1) == 0) panel_gemm<T, UPPER, true>(rs, ld, n, k, w, RS, wave, l16, g, pb);
+                else panel_gemm<T, UPPER, false>(rs, ld, n, k, w, RS, wave, l16, g, pb);
             } else {
-                panel_gemm<R, UPPER, false>(rs, ld, n, k, w, RS, wave, l16, g, pb);
+                panel_gemm<T, UPPER, false>(rs, ld, n, k, w, RS, wave, l16, g, pb);
             }
             __syncthreads();
 
             // ---- (ii) factor and invert the diagonal block on wave 0
-            if (wave == 0) factor_invert<R, UPPER>(pb, wm, colx, lane, k, n, w, rs, ld, *s_inf);
+            if (wave == 0) {
+                if constexpr (CPLX) factor_invert_inplace<T, UPPER>(pb, wm, rdiag, lane, k, n, w, rs, ld, *s_inf);
+                else factor_invert<T, UPPER>(pb, wm, colx, rdiag, lane, k, n, w, rs, ld, *s_inf);
+            }
             __syncthreads();
 
-            // ---- (iii) rows below the diagonal block: L21 = P21 W^T on MFMA,
-            // with P21 (rows) and W^T (columns) read from LDS
+            // ---- (iii) rows below the diagonal block: L21 = P21 W^H on MFMA,
+            // with P21 (rows) and conj(W) (columns) read from LDS
+            asm volatile("" : "+v"(lane));   // (addresses of the solve are formed here)
+            const int l16s = lane & 15, gs = lane >> 4;
             static_for<0, MAXT>([&](auto tt) {
                 constexpr int t = tt;
                 const int ib = wave + WAVES * t;
@@ -338,19 +459,24 @@ __global__ __launch_bounds__(64 * WAVES) void potrf_blocked_kernel(
                     static_for<0, 2>([&](auto pp) {
                         constexpr int cbp = pp;
                         v4 x = {R(0), R(0), R(0), R(0)};
+                        v4 xi = {R(0), R(0), R(0), R(0)};
                         static_for<0, 4 * (cbp + 1)>([&](auto uu) {   // W is lower triangular
                             constexpr int u = uu;
-                            const int c = 4 * u + g;                  // contraction index
-                            const R ao = pb[(ib * 16 + l16) * LDD + c];
-                            const R bo = wm[(cbp * 16 + l16) * LDD + c];
-                            x = M::mac(ao, bo, x);
+                            const int c = 4 * u + gs;                  // contraction index
+                            const T ao = pb[(ib * 16 + l16s) * LDD + c];
+                            const T bo = wm[(cbp * 16 + l16s) * LDD + c];
+                            if constexpr (CPLX) cmac<false>(ao.re, ao.im, bo.re, bo.im, x, xi);
+                            else x = M::mac(ao, bo, x);
                         });
                         static_for<0, 4>([&](auto rr) {
                             constexpr int r = rr;
-                            const int row = k + ib * 16 + M::row(r, g);
-                            const int col = cbp * 16 + l16;
+                            const int row = k + ib * 16 + M::row(r, gs);
+                            const int col = cbp * 16 + l16s;
                             const bool st = row < n && col < w;
-                            buf_store<R>(rs, st ? off(row, k + col) : kBufOOB, x[r]);
+                            T val;
+                            if constexpr (CPLX) val = T{x[r], UPPER ? -xi[r] : xi[r]};
+                            else val = x[r];
+                            buf_store<T>(rs, st ? off(row, k + col) : kBufOOB, val);
                         });
                     });
                 }
@@ -365,44 +491,48 @@ __global__ __launch_bounds__(64 * WAVES) void potrf_blocked_kernel(
 // ---------------------------------------------------------------- host side
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
 
-template <typename R>
+template <typename T>
 constexpr int64_t lds_bytes() {
-    return int64_t(MAXN * LDD + NBP * LDD) * sizeof(R) + 4 * NBP * 8 + 16;
+    using C = typename FactorType<T>::type;
+    using Rc = typename Traits<C>::R;
+    return int64_t(Shape<T>::MAXN * LDD + NBP * LDD) * sizeof(T) + 2 * NBP * sizeof(C) +
+           NBP * sizeof(Rc) + 16;
 }
 
-template <typename R>
+template <typename T>
 bool supported_t(int n, int64_t lda) {
-    return n >= 1 && n <= MAXN && lda * int64_t(n) * int64_t(sizeof(R)) < (int64_t(1) << 31);
+    return n >= 1 && n <= Shape<T>::MAXN && lda * int64_t(n) * int64_t(sizeof(T)) < (int64_t(1) << 31);
 }
 
-template <typename R>
+template <typename T>
 bool geometry_t(int n, int64_t batch, Geometry& g) {
-    if (n < 1 || n > MAXN) return false;
+    if (n < 1 || n > Shape<T>::MAXN) return false;
     g.family = FAM_BLOCKED;
     g.P = g.R = g.G = 0;
     g.threads = 64 * WAVES;
     g.panel = NBP;
     g.grid = batch < kMaxGrid ? batch : kMaxGrid;
-    g.lds = lds_bytes<R>();
+    g.lds = lds_bytes<T>();
     return true;
 }
 
-template <typename R>
+template <typename T>
 hipError_t potrf_t(bool upper, int n, void* A, int64_t lda, int64_t stride, int64_t batch,
                    int32_t* info, hipStream_t s) {
+    static_assert(lds_bytes<T>() <= 160 * 1024, "LDS per workgroup");
     const dim3 gd((unsigned)(batch < kMaxGrid ? batch : kMaxGrid)), bd(64 * WAVES);
-    R* a = static_cast<R*>(A);
-    const size_t shm = size_t(lds_bytes<R>());
+    T* a = static_cast<T*>(A);
+    const size_t shm = size_t(lds_bytes<T>());
     if (upper) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(potrf_blocked_kernel<R, true>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(potrf_blocked_kernel<T, true>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, int(shm));
         if (e != hipSuccess) return e;
-        return launch(potrf_blocked_kernel<R, true>, gd, bd, shm, s, a, n, lda, stride, batch, info);
+        return launch(potrf_blocked_kernel<T, true>, gd, bd, shm, s, a, n, lda, stride, batch, info);
     }
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(potrf_blocked_kernel<R, false>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(potrf_blocked_kernel<T, false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(shm));
     if (e != hipSuccess) return e;
-    return launch(potrf_blocked_kernel<R, false>, gd, bd, shm, s, a, n, lda, stride, batch, info);
+    return launch(potrf_blocked_kernel<T, false>, gd, bd, shm, s, a, n, lda, stride, batch, info);
 }
 
 }  // namespace blocked_detail

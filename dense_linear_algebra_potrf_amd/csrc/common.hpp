@@ -205,28 +205,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, kBufFlags);
 }
 
+// soff is a wave-uniform byte offset (a scalar register) added to off; only off
+// takes part in the range check, so a masked off stays out of range.
 template <typename T>
-__device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+__device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
     if constexpr (sizeof(T) == 4) {
-        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
     } else if constexpr (sizeof(T) == 8) {
-        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
     } else {
         static_assert(sizeof(T) == 16, "element size");
-        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
     }
 }
 
 template <typename T>
-__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off, const T& v) {
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off, const T& v,
+                                          uint32_t soff = 0) {
     if constexpr (sizeof(T) == 4) {
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, soff, 0);
     } else if constexpr (sizeof(T) == 8) {
         using V = uint32_t __attribute__((ext_vector_type(2)));
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(V, v), r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(V, v), r, off, soff, 0);
     } else {
         using V = uint32_t __attribute__((ext_vector_type(4)));
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(V, v), r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(V, v), r, off, soff, 0);
     }
 }
 

@@ -33,7 +33,7 @@ struct Geometry {
 // --- tiny: registers, P lanes x R rows per matrix, 64/P matrices per wavefront
 int tiny_max_n(DT dt);
 bool tiny_layout_ok(DT dt, int n, int64_t stride);   // byte offsets of a wave fit in 31 bits
-bool tiny_geometry(DT dt, int n, int64_t batch, Geometry& g);
+bool tiny_geometry(DT dt, bool upper, int n, int64_t lda, int64_t stride, int64_t batch, Geometry& g);
 hipError_t tiny_potrf(DT dt, bool upper, int n, void* A, int64_t lda, int64_t stride,
                       int64_t batch, int32_t* info, hipStream_t s);
 
@@ -41,7 +41,7 @@ hipError_t tiny_potrf(DT dt, bool upper, int n, void* A, int64_t lda, int64_t st
 int posv_tiny_max_n(DT dt);
 int posv_tiny_max_nrhs();
 bool posv_tiny_layout_ok(DT dt, int n, int64_t strideA, int64_t strideB);
-bool posv_tiny_geometry(DT dt, int n, int nrhs, int64_t batch, Geometry& g);
+bool posv_tiny_geometry(DT dt, bool upper, int n, int nrhs, int64_t lda, int64_t stride, int64_t batch, Geometry& g);
 hipError_t posv_tiny(DT dt, bool upper, int n, int nrhs, void* A, int64_t lda, int64_t strideA,
                      void* B, int64_t ldb, int64_t strideB, int64_t batch, int32_t* info,
                      hipStream_t s);

@@ -5,8 +5,8 @@ namespace bl {
 
 int posv_tiny_max_n_f32() { return tiny_detail::last_nb(tiny_detail::PosvConfigs<float>::type{}); }
 
-bool posv_tiny_geometry_f32(int n, int64_t batch, Geometry& g) {
-    return tiny_detail::geometry_t<float, tiny_detail::PosvConfigs<float>::type>(n, batch, g);
+bool posv_tiny_geometry_f32(bool upper, int n, int64_t lda, int64_t stride, int64_t batch, Geometry& g) {
+    return tiny_detail::geometry_t<float, tiny_detail::PosvConfigs<float>::type>(upper, n, lda, stride, batch, g);
 }
 
 bool posv_tiny_layout_ok_f32(int n, int64_t strideA, int64_t strideB) {

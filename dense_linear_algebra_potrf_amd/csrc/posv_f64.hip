@@ -5,8 +5,8 @@ namespace bl {
 
 int posv_tiny_max_n_f64() { return tiny_detail::last_nb(tiny_detail::PosvConfigs<double>::type{}); }
 
-bool posv_tiny_geometry_f64(int n, int64_t batch, Geometry& g) {
-    return tiny_detail::geometry_t<double, tiny_detail::PosvConfigs<double>::type>(n, batch, g);
+bool posv_tiny_geometry_f64(bool upper, int n, int64_t lda, int64_t stride, int64_t batch, Geometry& g) {
+    return tiny_detail::geometry_t<double, tiny_detail::PosvConfigs<double>::type>(upper, n, lda, stride, batch, g);
 }
 
 bool posv_tiny_layout_ok_f64(int n, int64_t strideA, int64_t strideB) {

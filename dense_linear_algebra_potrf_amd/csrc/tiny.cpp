@@ -5,11 +5,11 @@ namespace bl {
 
 #define BL_DECLARE_TINY(suf)                                                                  \
     int tiny_max_n_##suf();                                                                   \
-    bool tiny_geometry_##suf(int n, int64_t batch, Geometry& g);                              \
+    bool tiny_geometry_##suf(bool upper, int n, int64_t lda, int64_t stride, int64_t batch, Geometry& g);                       \
     bool tiny_layout_ok_##suf(int n, int64_t stride);                                         \
     bool posv_tiny_layout_ok_##suf(int n, int64_t strideA, int64_t strideB);                  \
     int posv_tiny_max_n_##suf();                                                              \
-    bool posv_tiny_geometry_##suf(int n, int64_t batch, Geometry& g);                         \
+    bool posv_tiny_geometry_##suf(bool upper, int n, int64_t lda, int64_t stride, int64_t batch, Geometry& g);                       \
     hipError_t posv_tiny_##suf(bool upper, int n, int nrhs, void* A, int64_t lda,             \
                                int64_t strideA, void* B, int64_t ldb, int64_t strideB,        \
                                int64_t batch, int32_t* info, hipStream_t s);                  \
@@ -41,12 +41,12 @@ bool tiny_layout_ok(DT dt, int n, int64_t stride) {
     return false;
 }
 
-bool tiny_geometry(DT dt, int n, int64_t batch, Geometry& g) {
+bool tiny_geometry(DT dt, bool upper, int n, int64_t lda, int64_t stride, int64_t batch, Geometry& g) {
     switch (dt) {
-    case DT::F32: return tiny_geometry_f32(n, batch, g);
-    case DT::F64: return tiny_geometry_f64(n, batch, g);
-    case DT::C64: return tiny_geometry_c64(n, batch, g);
-    case DT::C128: return tiny_geometry_c128(n, batch, g);
+    case DT::F32: return tiny_geometry_f32(upper, n, lda, stride, batch, g);
+    case DT::F64: return tiny_geometry_f64(upper, n, lda, stride, batch, g);
+    case DT::C64: return tiny_geometry_c64(upper, n, lda, stride, batch, g);
+    case DT::C128: return tiny_geometry_c128(upper, n, lda, stride, batch, g);
     }
     return false;
 }
@@ -84,14 +84,14 @@ bool posv_tiny_layout_ok(DT dt, int n, int64_t strideA, int64_t strideB) {
     return false;
 }
 
-bool posv_tiny_geometry(DT dt, int n, int nrhs, int64_t batch, Geometry& g) {
+bool posv_tiny_geometry(DT dt, bool upper, int n, int nrhs, int64_t lda, int64_t stride, int64_t batch, Geometry& g) {
     if (nrhs < 1 || nrhs > posv_tiny_max_nrhs()) return false;
     bool ok = false;
     switch (dt) {
-    case DT::F32: ok = posv_tiny_geometry_f32(n, batch, g); break;
-    case DT::F64: ok = posv_tiny_geometry_f64(n, batch, g); break;
-    case DT::C64: ok = posv_tiny_geometry_c64(n, batch, g); break;
-    case DT::C128: ok = posv_tiny_geometry_c128(n, batch, g); break;
+    case DT::F32: ok = posv_tiny_geometry_f32(upper, n, lda, stride, batch, g); break;
+    case DT::F64: ok = posv_tiny_geometry_f64(upper, n, lda, stride, batch, g); break;
+    case DT::C64: ok = posv_tiny_geometry_c64(upper, n, lda, stride, batch, g); break;
+    case DT::C128: ok = posv_tiny_geometry_c128(upper, n, lda, stride, batch, g); break;
     }
     if (!ok) return false;
     g.family = FAM_POSV_TINY;

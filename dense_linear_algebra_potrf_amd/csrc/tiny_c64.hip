@@ -8,8 +8,8 @@ int tiny_max_n_c64() { return tiny_detail::last_nb(tiny_detail::TinyConfigs<cflo
 
 bool tiny_layout_ok_c64(int n, int64_t stride) { return tiny_detail::layout_ok_t<cfloat>(n, stride); }
 
-bool tiny_geometry_c64(int n, int64_t batch, Geometry& g) {
-    return tiny_detail::geometry_t<cfloat>(n, batch, g);
+bool tiny_geometry_c64(bool upper, int n, int64_t lda, int64_t stride, int64_t batch, Geometry& g) {
+    return tiny_detail::geometry_t<cfloat>(upper, n, lda, stride, batch, g);
 }
 
 hipError_t tiny_potrf_c64(bool upper, int n, void* A, int64_t lda, int64_t stride, int64_t batch,

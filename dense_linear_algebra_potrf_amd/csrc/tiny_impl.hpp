@@ -72,8 +72,8 @@ __device__ __forceinline__ void tiny_solves(const T (&a)[R][P * R], const typena
     static_for<0, R>([&](auto rr) {
         static_for<0, NRHS>([&](auto kk) {
             constexpr int r = rr, k = kk;
-            const uint32_t off = (k < nrhs) ? boff[r] + uint32_t(k) * ldb_b : kBufOOB;
-            y[r][k] = buf_load<T>(rb, off);
+            const uint32_t off = (k < nrhs) ? boff[r] : kBufOOB;
+            y[r][k] = buf_load<T>(rb, off, uint32_t(k) * ldb_b);
             yf[r][k] = zero<T>();
         });
     });
@@ -140,34 +140,77 @@ __device__ __forceinline__ void tiny_solves(const T (&a)[R][P * R], const typena
     static_for<0, R>([&](auto rr) {
         static_for<0, NRHS>([&](auto kk) {
             constexpr int r = rr, k = kk;
-            const uint32_t off = (inf == 0 && k < nrhs) ? boff[r] + uint32_t(k) * ldb_b : kBufOOB;
-            buf_store<T>(rb, off, xf[r][k]);
+            const uint32_t off = (inf == 0 && k < nrhs) ? boff[r] : kBufOOB;
+            buf_store<T>(rb, off, xf[r][k], uint32_t(k) * ldb_b);
         });
     });
 }
 
+// Packed path: each matrix's image in LDS starts at a multiple of IMGP
+// elements, IMGP >= n*n with IMGP = P (mod 32), so that the partitions of a
+// wave read from different LDS banks.
+template <int P, int R>
+constexpr int packed_pitch() {
+    return (P * R) * (P * R) + (((P - (P * R) * (P * R)) % 32) + 32) % 32;
+}
+// Words of LDS for the image: every partition (the dead tail one included)
+// plus one more matrix, where steps past the run land.
+template <typename T, int P, int R>
+constexpr int packed_image_words() {
+    return (63 / P + 2) * packed_pitch<P, R>() * words<T>();
+}
+// Where the packed path is used (fp32 only), from timings of both variants on
+// MI355X over orders 8..33.  Lower: the rows of one column are contiguous,
+// so the per-row loads are already coalesced over a lane group, and the
+// packed path only wins for the smallest windows (order <= 12).  Upper: a
+// lane's row is a column of A, the per-row loads are strided across lanes,
+// and the packed path wins while its image stays small (<= 12 KiB per wave,
+// orders up to 18); beyond that the image limits the wavefronts per CU.
+constexpr int kPackedLowerMaxOrder = 12;
+constexpr int kPackedUpperMaxBytes = 12 * 1024;
+
 // NRHS = 0: potrf.  NRHS > 0: posv for up to NRHS right-hand sides (nrhs at
 // run time), with the factor kept in registers for both triangular solves.
-template <typename T, int P, int R, bool UPPER, int NRHS>
-__global__ __launch_bounds__(64 * kTinyWaves) void potrf_tiny_kernel(
-    T* __restrict__ A, int n, int64_t lda, int64_t stride, int64_t batch,
+//
+// PACKED (n = P R exactly, lda = n, stride = n*n, so a wavefront's G matrices
+// are one contiguous run of memory): the referenced triangle is moved between
+// HBM and registers through an LDS image of the wave's matrices, with
+// consecutive lanes on consecutive elements, so every load and store
+// instruction covers 64 consecutive elements.  Each element's (row, column,
+// matrix) is tracked incrementally along the run; whether it is referenced is
+// kept as one bit per element and lane, used again by the stores, so the other
+// triangle is neither read nor written.  With n known at compile time, every
+// LDS address of a row is a register plus an immediate offset.  The
+// pivot-column exchange buffer reuses the image once the rows have been read
+// out of it.  One wavefront per workgroup.  Otherwise each lane loads and
+// stores its own rows (any order n <= P R, any layout).
+template <typename T, int P, int R, bool UPPER, int NRHS, bool PACKED>
+__global__ __launch_bounds__(PACKED ? 64 : 64 * kTinyWaves) void potrf_tiny_kernel(
+    T* __restrict__ A, int n_arg, int64_t lda, int64_t stride, int64_t batch,
     int32_t* __restrict__ info, T* __restrict__ B, int nrhs, int64_t ldb, int64_t strideB)
 {
+    const int n = PACKED ? P * R : n_arg;
     using Rt = typename Traits<T>::R;
     constexpr int NB = P * R;
     constexpr int G = 64 / P;
     constexpr int PARTS = 63 / P + 1;     // includes a partial, dead tail partition
     constexpr int D = words<T>();
     constexpr int ROWW = tiny_row_words(NB + NRHS, D);
-    __shared__ __attribute__((aligned(16))) uint32_t lds[kTinyWaves][2][PARTS][ROWW];
+    constexpr int WAVES = PACKED ? 1 : kTinyWaves;
+    constexpr int XW = 2 * PARTS * ROWW;                          // exchange words per wave
+    constexpr int IMGW = PACKED ? packed_image_words<T, P, R>() : 0;
+    constexpr int LDSW = XW > IMGW ? XW : IMGW;
+    __shared__ __attribute__((aligned(16))) uint32_t lds_raw[WAVES][LDSW];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int p = lane / P;
     const int q = lane - p * P;
-    const int64_t b_first = ((int64_t)blockIdx.x * kTinyWaves + wave) * G;   // wave-uniform
+    const int64_t b_first = ((int64_t)blockIdx.x * WAVES + wave) * G;   // wave-uniform
     const int64_t b = b_first + p;
     const bool live = (p < G) && (b < batch);
+    uint32_t* const xbuf = &lds_raw[wave][0];
+    auto xrow = [&](int par, int part) -> uint32_t* { return xbuf + (par * PARTS + part) * ROWW; };
     // One buffer descriptor per wavefront; the host guarantees every byte offset
     // inside the wave's G matrices is below 2^31.  Masked elements use an
     // out-of-range offset, so they are neither read nor written.
@@ -189,19 +232,96 @@ __global__ __launch_bounds__(64 * kTinyWaves) void potrf_tiny_kernel(
     // S(i, c) for c <= i: A(i, c) for Lower, conj(A(c, i)) for Upper.  Rows at
     // or beyond n, and dead partitions, hold the identity.
     T a[R][NB];
+    // packed path: element e of the wave's run is matrix ep, column ec, row ei
+    constexpr int K = cdiv(G * NB * NB, 64);       // 64-element steps over the run
+    constexpr int NBITS = cdiv(K, 32);
+    constexpr int NN = NB * NB;
+    constexpr int IMGP = packed_pitch<P, R>();
+    uint32_t refbits[NBITS > 0 ? NBITS : 1];
+    const int glive = int(batch - b_first < G ? batch - b_first : G);
+    // masked offset: bit 31 puts a lane out of the buffer's range
+    auto masked = [&](uint32_t o, bool ok) -> uint32_t { return o | (uint32_t(!ok) << 31); };
+    // walks the run 64 elements at a time: element e = 64 v + lane is matrix
+    // ep, column ec, row ei; calls f(v, e, image index, referenced)
+    auto walk = [&](auto f, auto chunked) {
+        // the lane index is hidden from the optimiser, so that the second walk
+        // recomputes its offsets instead of keeping the first walk's live
+        // across the factorisation
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        int ep = ln / NN;
+        const int erem = ln - ep * NN;
+        int ec = erem / NB;
+        int ei = erem - ec * NB;
+        constexpr int DI = 64 % NB, DQ = 64 / NB, DC = DQ % NB, DP = DQ / NB;
+        static_for<0, K>([&](auto vv) {
+            constexpr int v = vv;
+            const int e = 64 * v + ln;
+            const bool ok = ep < glive && (UPPER ? ei <= ec : ei >= ec);
+            f(vv, e, e + ep * (IMGP - NN), ok);
+            // the stores go out 16 at a time: otherwise every LDS read and
+            // offset of the run is computed first and held in registers
+            if constexpr (decltype(chunked)::value && v % 16 == 15) __builtin_amdgcn_sched_barrier(0);
+            ei += DI;
+            const bool ci = ei >= NB;
+            ei = ci ? ei - NB : ei;
+            ec += DC + (ci ? 1 : 0);
+            const bool cc = ec >= NB;
+            ec = cc ? ec - NB : ec;
+            ep += DP + (cc ? 1 : 0);
+        });
+    };
+    // image element of slot (r, c) of this lane's rows: element (i, c) of the
+    // matrix for Lower, element (c, i) for Upper (i = q + r P)
+    const int rowbase = UPPER ? p * IMGP + q * NB : p * IMGP + q;
+    auto img_index = [&](int r, int c) -> int {
+        return UPPER ? rowbase + (r * P) * NB + c : rowbase + r * P + c * NB;
+    };
+    if constexpr (PACKED) {
+        static_for<0, NBITS>([&](auto ww) { refbits[ww] = 0u; });
+        walk([&](auto vv, int e, int idx, bool ok) {
+            constexpr int v = vv;
+            refbits[v / 32] |= uint32_t(ok) << (v % 32);
+            const T x = buf_load<T>(rsrc, masked(uint32_t(e) * S, ok));
+            lds_put<T>(xbuf, idx, x);
+        }, std::false_type{});
+        wave_lds_sync();
+    }
     static_for<0, R>([&](auto rr) {
         constexpr int r = rr;
         const int i = q + r * P;
         static_for<0, cmin(NB, (r + 1) * P)>([&](auto cc) {
             constexpr int c = cc;
-            uint32_t off = elem_off(r, c);
-            if constexpr (c >= r * P) off = (c <= i) ? off : kBufOOB;   // diagonal block
-            T v = buf_load<T>(rsrc, off);
-            if constexpr (UPPER) v = conj(v);
-            if constexpr (c >= r * P) v = select(c == i && roff[r] == kBufOOB, one<T>(), v);
+            T v;
+            if constexpr (PACKED) {
+                // rows of dead partitions read an unused image region; the
+                // select below turns them (and padding) into the identity
+                v = lds_get<T>(xbuf, img_index(r, c));
+                v = select(live, v, zero<T>());
+            } else {
+                // Lower: the column offset goes in the scalar offset, so
+                // each load needs no address register of its own
+                uint32_t off = UPPER ? elem_off(r, c) : roff[r];
+                if constexpr (c >= r * P) off = (c <= i) ? off : kBufOOB;   // diagonal block
+                v = buf_load<T>(rsrc, off, UPPER ? 0u : uint32_t(c) * lda_b);
+            }
             a[r][c] = v;
         });
     });
+    // Every load is issued before the first use of a loaded value: otherwise
+    // the scheduler may place each select right after its load and wait for
+    // the loads one at a time.
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, R>([&](auto rr) {
+        constexpr int r = rr;
+        const int i = q + r * P;
+        static_for<0, cmin(NB, (r + 1) * P)>([&](auto cc) {
+            constexpr int c = cc;
+            if constexpr (UPPER) a[r][c] = conj(a[r][c]);
+            if constexpr (c >= r * P) a[r][c] = select(c == i && roff[r] == kBufOOB, one<T>(), a[r][c]);
+        });
+    });
+    if constexpr (PACKED) wave_lds_sync();   // the exchange buffer reuses the image
 
     // Register slots a[r][k] with k > i (the row's upper part) are scratch: they
     // absorb updates but never feed a referenced slot, so a step needs no
@@ -212,15 +332,16 @@ __global__ __launch_bounds__(64 * kTinyWaves) void potrf_tiny_kernel(
     // by then and info keeps the first failing column.
     //
     // Look-ahead: within step j, column j+1 is updated first and published to
-    // LDS, and its 16-byte broadcast reads are issued before the rest of step
-    // j's updates, so the exchange latency hides behind that arithmetic.
-    // Column j is published at slots relative to j (row i -> slot i - j), so
-    // the entries a step needs always start at slot 0: 16-byte aligned reads,
-    // fewer of them as j grows.  Rows above j write to a spare slot at NB.
+    // LDS before the rest of step j's updates, so the exchange latency hides
+    // behind that arithmetic.  Column j is published at slots relative to j
+    // (row i -> slot i - j), so the entries a step needs always start at slot
+    // 0; a step reads them from LDS where it uses them (broadcast reads), so no
+    // copy of the column is held in registers.  Rows above j write to a spare
+    // slot at NB.
     auto publish = [&](auto jc) {
         constexpr int j = decltype(jc)::value;
         constexpr int rj = j / P;
-        uint32_t* row = &lds[wave][j & 1][p][0];
+        uint32_t* row = xrow(j & 1, p);
         static_for<rj, R>([&](auto rr) {
             constexpr int r = rr;
             const int i = q + r * P;
@@ -228,35 +349,19 @@ __global__ __launch_bounds__(64 * kTinyWaves) void potrf_tiny_kernel(
             lds_put<T>(row, slot, a[r][j]);
         });
     };
-    auto fetch = [&](auto jc, uint32_t (&w)[ROWW]) {
-        constexpr int j = decltype(jc)::value;
-        const uint4* row4 = reinterpret_cast<const uint4*>(
-            __builtin_assume_aligned(&lds[wave][j & 1][p][0], 16));
-        static_for<0, cdiv((NB - j) * D, 4)>([&](auto vv) {
-            constexpr int v = vv;
-            const uint4 x = row4[v];
-            w[4 * v + 0] = x.x;
-            w[4 * v + 1] = x.y;
-            w[4 * v + 2] = x.z;
-            w[4 * v + 3] = x.w;
-        });
-    };
-    // entry for row k of column j (k >= j) in a fetched column
-    auto colv = [&](const uint32_t (&w)[ROWW], int j, int k) -> T {
-        return from_words<T>(&w[(k - j) * D]);
-    };
+    // entry for row k of column j (k >= j), read from the published column
+    // (the buffer of column j is not overwritten before step j + 2)
+    auto colv = [&](int j, int k) -> T { return lds_get<T>(xrow(j & 1, p), k - j); };
 
     int32_t inf = 0;
     Rt invd[R];                 // 1 / L(i, i) of each held row (used by the solves)
     static_for<0, R>([&](auto rr) { invd[rr] = Rt(1); });
-    uint32_t wcur[ROWW];
     publish(ic<0>{});
     wave_lds_sync();
-    fetch(ic<0>{}, wcur);
     static_for<0, NB>([&](auto jj) {
         constexpr int j = jj;
         constexpr int rj = j / P;
-        const Rt d = re(colv(wcur, j, j));
+        const Rt d = re(colv(j, j));
         inf = (inf == 0 && !(d > Rt(0))) ? (j + 1) : inf;
         const Rt inv = pivot_rcp(d);
         const Rt rs = pivot_rsq(d);
@@ -265,23 +370,22 @@ __global__ __launch_bounds__(64 * kTinyWaves) void potrf_tiny_kernel(
             constexpr int r = rr;
             t[r] = scale(a[r][j], inv);
         });
-        uint32_t wnext[ROWW];
         if constexpr (j + 1 < NB) {
             constexpr int rn = (j + 1) / P;
+            const T cj1 = colv(j, j + 1);
             static_for<rn, R>([&](auto rr) {
                 constexpr int r = rr;
-                sub_mul_conj(a[r][j + 1], t[r], colv(wcur, j, j + 1));
+                sub_mul_conj(a[r][j + 1], t[r], cj1);
             });
             publish(ic<j + 1>{});
             wave_lds_sync();
-            fetch(ic<j + 1>{}, wnext);
         }
         static_for<rj, R>([&](auto rr) {
             constexpr int r = rr;
             constexpr int kend = cmin(NB, (r + 1) * P);
             static_for<j + 2, kend>([&](auto kk) {
                 constexpr int k = kk;
-                sub_mul_conj(a[r][k], t[r], colv(wcur, j, k));
+                sub_mul_conj(a[r][k], t[r], colv(j, k));
             });
             if constexpr (r == rj) {
                 // the one row block that holds row j itself
@@ -292,29 +396,45 @@ __global__ __launch_bounds__(64 * kTinyWaves) void potrf_tiny_kernel(
                 a[r][j] = scale(a[r][j], rs);
             }
         });
-        if constexpr (j + 1 < NB) {
-            static_for<0, 4 * cdiv((NB - j - 1) * D, 4)>([&](auto kk) {
-                constexpr int k = kk;
-                wcur[k] = wnext[k];
-            });
-        }
     });
 
     if constexpr (NRHS > 0)
-        tiny_solves<T, P, R, NRHS>(a, invd, &lds[wave][0][0][0], PARTS * ROWW, ROWW, p, q, live, n,
+        tiny_solves<T, P, R, NRHS>(a, invd, xbuf, PARTS * ROWW, ROWW, p, q, live, n,
                                    inf, B + b_first * strideB, nrhs, ldb, strideB);
 
-    static_for<0, R>([&](auto rr) {
-        constexpr int r = rr;
-        const int i = q + r * P;
-        static_for<0, cmin(NB, (r + 1) * P)>([&](auto cc) {
-            constexpr int c = cc;
-            uint32_t off = elem_off(r, c);
-            if constexpr (c >= r * P) off = (c <= i) ? off : kBufOOB;
-            if constexpr (UPPER) buf_store<T>(rsrc, off, conj(a[r][c]));
-            else buf_store<T>(rsrc, off, a[r][c]);
+    if constexpr (PACKED) {
+        // rows back into the image (every lane writes; slots that are not
+        // referenced elements go to the spare element), then the run back to HBM
+        wave_lds_sync();
+        // every slot is written back to its own image position: slots right of
+        // the diagonal land on elements of the other triangle, which the run's
+        // stores skip, and dead partitions write into their unused regions
+        static_for<0, R>([&](auto rr) {
+            constexpr int r = rr;
+            static_for<0, cmin(NB, (r + 1) * P)>([&](auto cc) {
+                constexpr int c = cc;
+                lds_put<T>(xbuf, img_index(r, c), UPPER ? conj(a[r][c]) : a[r][c]);
+            });
         });
-    });
+        wave_lds_sync();
+        walk([&](auto vv, int e, int idx, bool) {
+            constexpr int v = vv;
+            const bool ok = (refbits[v / 32] >> (v % 32)) & 1u;
+            buf_store<T>(rsrc, masked(uint32_t(e) * S, ok), lds_get<T>(xbuf, idx));
+        }, std::true_type{});
+    } else {
+        static_for<0, R>([&](auto rr) {
+            constexpr int r = rr;
+            const int i = q + r * P;
+            static_for<0, cmin(NB, (r + 1) * P)>([&](auto cc) {
+                constexpr int c = cc;
+                uint32_t off = UPPER ? elem_off(r, c) : roff[r];
+                if constexpr (c >= r * P) off = (c <= i) ? off : kBufOOB;
+                if constexpr (UPPER) buf_store<T>(rsrc, off, conj(a[r][c]));
+                else buf_store<T>(rsrc, off, a[r][c], uint32_t(c) * lda_b);
+            });
+        });
+    }
     if (live && q == 0 && info != nullptr) info[b] = inf;
 }
 
@@ -327,8 +447,8 @@ template <typename... Cs> struct TList {};
 // Ordered by order served (NB); the first entry with NB >= n is used.
 template <typename T> struct TinyConfigs;
 template <> struct TinyConfigs<float> {
-    using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<9, 2>, TC<8, 3>, TC<8, 4>,
-                       TC<11, 3>>;
+    using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<17, 1>, TC<9, 2>, TC<8, 3>,
+                       TC<16, 2>, TC<11, 3>>;
 };
 template <> struct TinyConfigs<double> {
     using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<8, 3>, TC<8, 4>>;
@@ -379,21 +499,58 @@ bool layout_ok_t(int n, int64_t stride) {
     return ok;
 }
 
+// The packed variant exists for fp32 (the element type of the bandwidth-bound
+// workloads) and is used when n is the configuration's own order and the
+// layout is packed.
+template <typename T, typename C, bool UPPER>
+constexpr bool packed_wanted() {
+    return std::is_same<T, float>::value &&
+           (UPPER ? packed_image_words<T, C::P, C::R>() * 4 <= kPackedUpperMaxBytes
+                  : C::NB <= kPackedLowerMaxOrder);
+}
+template <typename C>
+inline bool packed_layout(int n, int64_t lda, int64_t stride) {
+    return n == C::NB && lda == n && stride == int64_t(n) * n;
+}
+
 template <typename T, typename List = typename TinyConfigs<T>::type>
-bool geometry_t(int n, int64_t batch, Geometry& g) {
+bool geometry_t(bool upper, int n, int64_t lda, int64_t stride, int64_t batch, Geometry& g) {
     return pick_config(List{}, n, [&](auto c) {
         using C = decltype(c);
         constexpr int G = 64 / C::P;
         constexpr int D = words<T>();
+        const bool packed = (upper ? packed_wanted<T, C, true>() : packed_wanted<T, C, false>()) &&
+                            packed_layout<C>(n, lda, stride);
+        const int waves = packed ? 1 : kTinyWaves;
+        const int64_t xw = int64_t(2) * (63 / C::P + 1) * tiny_row_words(C::NB, D);
+        const int64_t iw = packed_image_words<T, C::P, C::R>();
         g.family = FAM_TINY;
         g.P = C::P;
         g.R = C::R;
         g.G = G;
-        g.threads = 64 * kTinyWaves;
+        g.threads = 64 * waves;
         g.panel = 0;
-        g.grid = (batch + G * kTinyWaves - 1) / (G * kTinyWaves);
-        g.lds = int64_t(kTinyWaves) * 2 * (63 / C::P + 1) * tiny_row_words(C::NB, D) * 4;
+        g.grid = (batch + G * waves - 1) / (G * waves);
+        g.lds = packed ? 4 * (xw > iw ? xw : iw) : int64_t(waves) * xw * 4;
     });
+}
+
+// One launch of the tiny kernel: the packed variant where the layout and the
+// image size allow it, the per-row variant otherwise.
+template <typename T, typename C, bool UPPER, int NRHS>
+hipError_t launch_tiny(int n, T* a, int64_t lda, int64_t stride, int64_t batch, int32_t* info,
+                       T* b, int nrhs, int64_t ldb, int64_t strideB, hipStream_t s) {
+    constexpr int G = 64 / C::P;
+    if constexpr (packed_wanted<T, C, UPPER>()) {
+        if (packed_layout<C>(n, lda, stride)) {
+            const int64_t grid = (batch + G - 1) / G;
+            return launch(potrf_tiny_kernel<T, C::P, C::R, UPPER, NRHS, true>, dim3((unsigned)grid),
+                          dim3(64), 0, s, a, n, lda, stride, batch, info, b, nrhs, ldb, strideB);
+        }
+    }
+    const int64_t grid = (batch + G * kTinyWaves - 1) / (G * kTinyWaves);
+    return launch(potrf_tiny_kernel<T, C::P, C::R, UPPER, NRHS, false>, dim3((unsigned)grid),
+                  dim3(64 * kTinyWaves), 0, s, a, n, lda, stride, batch, info, b, nrhs, ldb, strideB);
 }
 
 template <typename T>
@@ -402,17 +559,12 @@ hipError_t potrf_t(bool upper, int n, void* A, int64_t lda, int64_t stride, int6
     hipError_t err = hipErrorInvalidValue;
     pick_config(typename TinyConfigs<T>::type{}, n, [&](auto c) {
         using C = decltype(c);
-        constexpr int G = 64 / C::P;
-        const int64_t grid = (batch + G * kTinyWaves - 1) / (G * kTinyWaves);
-        const dim3 gd((unsigned)grid), bd(64 * kTinyWaves);
         T* a = static_cast<T*>(A);
         T* nob = nullptr;
         if (upper)
-            err = launch(potrf_tiny_kernel<T, C::P, C::R, true, 0>, gd, bd, 0, s, a, n, lda, stride,
-                         batch, info, nob, 0, int64_t(0), int64_t(0));
+            err = launch_tiny<T, C, true, 0>(n, a, lda, stride, batch, info, nob, 0, 0, 0, s);
         else
-            err = launch(potrf_tiny_kernel<T, C::P, C::R, false, 0>, gd, bd, 0, s, a, n, lda, stride,
-                         batch, info, nob, 0, int64_t(0), int64_t(0));
+            err = launch_tiny<T, C, false, 0>(n, a, lda, stride, batch, info, nob, 0, 0, 0, s);
     });
     return err;
 }
@@ -438,20 +590,14 @@ hipError_t posv_t(bool upper, int n, int nrhs, void* A, int64_t lda, int64_t str
     hipError_t err = hipErrorInvalidValue;
     pick_config(typename PosvConfigs<T>::type{}, n, [&](auto c) {
         using C = decltype(c);
-        constexpr int G = 64 / C::P;
-        const int64_t grid = (batch + G * kTinyWaves - 1) / (G * kTinyWaves);
-        const dim3 gd((unsigned)grid), bd(64 * kTinyWaves);
         T* a = static_cast<T*>(A);
         T* bb = static_cast<T*>(B);
-        auto go = [&](auto kern) {
-            err = launch(kern, gd, bd, 0, s, a, n, lda, strideA, batch, info, bb, nrhs, ldb, strideB);
-        };
         if (nrhs == 1) {
-            if (upper) go(potrf_tiny_kernel<T, C::P, C::R, true, 1>);
-            else go(potrf_tiny_kernel<T, C::P, C::R, false, 1>);
+            if (upper) err = launch_tiny<T, C, true, 1>(n, a, lda, strideA, batch, info, bb, nrhs, ldb, strideB, s);
+            else err = launch_tiny<T, C, false, 1>(n, a, lda, strideA, batch, info, bb, nrhs, ldb, strideB, s);
         } else {
-            if (upper) go(potrf_tiny_kernel<T, C::P, C::R, true, kPosvMaxRhs>);
-            else go(potrf_tiny_kernel<T, C::P, C::R, false, kPosvMaxRhs>);
+            if (upper) err = launch_tiny<T, C, true, kPosvMaxRhs>(n, a, lda, strideA, batch, info, bb, nrhs, ldb, strideB, s);
+            else err = launch_tiny<T, C, false, kPosvMaxRhs>(n, a, lda, strideA, batch, info, bb, nrhs, ldb, strideB, s);
         }
     });
     return err;

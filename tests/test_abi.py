@@ -116,6 +116,17 @@ def test_route_auto_picks_by_size(lib):
     assert bl.route("f32", "L", 8, 1024)["family"] == "tiny"
     assert bl.route("f32", "L", 17, 32768)["family"] == "tiny"
     assert bl.route("c128", "U", 16, 64)["family"] == "tiny"
+    # above the LDS family's capacity the complex types go to the blocked family
+    assert bl.route("c64", "U", 128, 64)["family"] == "blocked"
+    assert bl.route("c64", "L", 512, 64)["family"] == "blocked"
+    assert bl.route("c128", "L", 256, 64)["family"] == "blocked"
+
+
+def test_route_beyond_every_family_is_not_supported(lib):
+    for dt, n in (("c128", 257), ("c64", 513), ("f64", 513), ("f32", 1000)):
+        with pytest.raises(bl.BatchlasError) as e:
+            bl.route(dt, "L", n, 4)
+        assert e.value.status_name == "NOT_SUPPORTED"
 
 
 def _route_in_subprocess(env_extra: dict, code: str) -> str:

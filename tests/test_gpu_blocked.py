@@ -42,10 +42,15 @@ def plant_at(a: np.ndarray, cols) -> np.ndarray:
     return want
 
 
-@pytest.mark.parametrize("dt", ["f32", "f64"])
+# largest order of the blocked family per element type (cdouble: the panel
+# buffer of 256 x 33 elements fills the LDS)
+MAXN = {"f32": 512, "f64": 512, "c64": 512, "c128": 256}
+
+
+@pytest.mark.parametrize("dt", ["f32", "f64", "c64", "c128"])
 @pytest.mark.parametrize("uplo", ["L", "U"])
 def test_blocked_orders(dt, uplo):
-    for n in ORDERS:
+    for n in [m for m in ORDERS if m <= MAXN[dt]]:
         batch = 6 if n > 256 else 11
         a = syn.spd_matrices(n, batch, dt, seed=40 * n + (uplo == "U"))
         cols = [None, 0, n // 2, n - 1, 31, 32, None, 33, 100, 63, 64][:batch]
@@ -53,10 +58,10 @@ def test_blocked_orders(dt, uplo):
         check_potrf(a, uplo, family="blocked", expect_info=want, label="blocked-orders")
 
 
-@pytest.mark.parametrize("dt", ["f32", "f64"])
+@pytest.mark.parametrize("dt", ["f32", "f64", "c64", "c128"])
 @pytest.mark.parametrize("uplo", ["L", "U"])
 def test_blocked_poison_and_padding(dt, uplo):
-    for n in (40, 100, 300):
+    for n in [m for m in (40, 100, 300) if m <= MAXN[dt]] + ([MAXN[dt]] if dt == "c128" else []):
         a = syn.spd_matrices(n, 5, dt, seed=n)
         plant_at(a, [None, 3, None, n - 2, None])
         for fill in (syn.nan_value(dt), syn.sentinel(dt)):
