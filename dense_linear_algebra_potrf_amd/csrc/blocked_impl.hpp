@@ -11,17 +11,19 @@
 //   for each panel of NBP = 32 columns starting at k:
 //     (i)   GEMM: P = S(k:n, k:k+32) - L(k:n, 0:k) L(k:k+32, 0:k)^T on MFMA
 //           (v_mfma_*_16x16x4, accumulated as L L^T - S so that no operand needs
-//           negating), each of 8 waves owning every eighth 32-row superblock;
-//           P is kept in LDS (up to 512 x 33 elements), so the accumulators
-//           are dead while the diagonal block is factored;
-//     (ii)  the 32 x 32 diagonal block of P is factored on one wave, and the
-//           inverse of its factor is built in the same sweep (every
-//           elimination step is also applied to the columns of the identity),
-//           info merged as k + j + 1;
+//           negating), the 32-row superblocks spread over 7 waves; P goes to
+//           LDS (up to 512 x 33 elements);
+//     (ii)  the 32 x 32 diagonal block of P is factored on wave 0, and the
+//           inverse W of its factor is formed column by column, info merged
+//           as k + j + 1;
 //     (iii) the rows below are solved by a second MFMA product
-//           L21 = P21 W^T with W = L11^-1 (lower triangular, zero blocks
-//           skipped), both operands read from LDS;
-//     then the panel is written to the matrix, where the next panels read it.
+//           L21 = P21 W^T (W lower triangular, zero blocks skipped), both
+//           operands read from LDS, and written to the matrix, where the next
+//           panels read them.
+//   Look-ahead: while wave 0 works on (ii) for panel k, the other 7 waves
+//   already run (i) for panel k + 32 over the columns left of k, which are
+//   final; after (iii) they add the 32 columns of panel k.  So the one-wave
+//   diagonal phase overlaps the bulk of the next GEMM.
 //
 // S = A for Lower, S(i, c) = conj(A(c, i)) for Upper; for the real types the
 // Upper form only swaps the address of each element.  The complex types run
@@ -233,57 +235,48 @@ __device__ __forceinline__ void factor_invert_inplace(T* pb, T* wm, typename Tra
     if (lane == 0) s_inf = inf;
 }
 
-// The GEMM of one panel: P = S(k:n, k:k+w) - L(k:n, 0:k) L(k:k+w, 0:k)^T,
-// accumulated on MFMA as L L^T - S (so no operand needs negating) and written,
-// negated back, into the panel buffer pb (row i of the panel at pb[i * LDD];
-// columns at or beyond w as 0).
+// The GEMM of one panel starting at column kp:
+//     P = S(kp:n, kp:kp+w) - L(kp:n, 0:kp) L(kp:kp+w, 0:kp)^H,
+// accumulated on MFMA as L L^H - S (so that no operand needs negating) and
+// written, negated back, into the panel buffer pb (row i of the panel at
+// pb[i * LDD]; columns at or beyond w as 0).  The contraction can be split:
+// accumulate() adds the columns [q0, q1) of L, so that the part over columns
+// that are already final can run before the previous panel is solved.
 //
-// MFMA roles: the A operand runs over the panel's columns c (rows k + c of L),
-// the B operand over the panel's rows i; the result is P^T tile by tile.  With
-// PAIRED, a lane loads rows 2 l16 and 2 l16 + 1 of one column with a single
-// 16-byte load; otherwise two 8-byte loads.  Either way every load is issued
-// unconditionally and masked through the out-of-range offset (rows at or
-// beyond n, steps past k).  Operands live in a ring of NS register sets, loads NS - 1
-// steps ahead of the MFMAs.
-template <typename T, bool UPPER, bool PAIRED>
-__device__ __forceinline__ void panel_gemm(__amdgpu_buffer_rsrc_t rs, uint32_t ld, int n, int k,
-                                           int w, int RS, int wave, int l16, int g, T* pb)
-{
+// The GW GEMM waves (gw = 0 .. GW-1) own the 32-row superblocks sb = gw + GW s
+// of the panel, each split into its even and odd rows (two 16-row MFMA tiles);
+// the panel's 32 columns are split the same way (cb = 0: even columns, cb = 1:
+// odd columns), so that a lane loads two consecutive rows of a column at once
+// where the layout allows it.  MFMA roles: the A operand runs over the panel's
+// columns c (rows kp + c of L), the B operand over the panel's rows i; the
+// result is P^T tile by tile.  With PAIRED (fp64 Lower, n even), a lane loads
+// rows 2 l16 and 2 l16 + 1 of one column with a single 16-byte load; otherwise
+// two loads.  Every load is issued unconditionally and masked through the
+// out-of-range offset (rows at or beyond n, steps past q1).  Operands live in
+// a ring of NS register sets, loads NS - 1 steps ahead of the MFMAs.  The
+// complex types keep the imaginary parts in aci; for Upper their arithmetic
+// runs on the stored values, conj(S) and conj(L), which gives conj(P), and the
+// conjugate is taken when P is written out.
+template <typename T, bool UPPER, bool PAIRED, int GW>
+struct PanelGemm {
     using R = typename Traits<T>::R;
-    constexpr bool CPLX = Traits<T>::cplx;
+    static constexpr bool CPLX = Traits<T>::cplx;
     using M = Mfma<R>;
     using v4 = typename M::v4;
-    constexpr uint32_t S = sizeof(T);
-    constexpr int MAXS = Shape<T>::MAXS;   // superblocks per wave
-    // ring depth (fp32 and the complex types: fewer, to stay within 256 registers)
-    constexpr int NS = (!CPLX && sizeof(R) == 8) ? 8 : 4;
-    auto off = [&](int row, int col) -> uint32_t {
-        return UPPER ? (uint32_t(row) * ld + uint32_t(col)) * S : (uint32_t(col) * ld + uint32_t(row)) * S;
-    };
-    // accumulators start from S(k:n, k:k+w) (referenced part only): tile
-    // (s, e, cb), register r holds column c = 2 row(r, g) + cb, row i = 32 sb + 2 l16 + e.
-    // The complex types keep the imaginary parts in aci.  For Upper the
-    // complex arithmetic runs on the stored values, conj(S) and conj(L), which
-    // gives conj(P); the conjugate is taken when P is written out.
+    static constexpr uint32_t S = sizeof(T);
+    static constexpr int MAXS = cdiv(Shape<T>::MAXN / 32, GW);   // superblocks per wave
+    // ring depth: as deep as 256 registers allow next to the accumulators
+    static constexpr int NS = 4;
     v4 acc[MAXS][2][2], aci[MAXS][2][2];
-    static_for<0, MAXS>([&](auto ss) {
-        constexpr int s = ss;
-        const int sb = wave + WAVES * s;
-        static_for<0, 2>([&](auto ee) {
-            static_for<0, 2>([&](auto cc) {
-                static_for<0, 4>([&](auto rr) {
-                    constexpr int e = ee, cb = cc, r = rr;
-                    const int c = 2 * M::row(r, g) + cb;
-                    const int i = 32 * sb + 2 * l16 + e;
-                    const bool ref = sb < RS && k + i < n && c < w && i >= c;
-                    const T x = buf_load<T>(rs, ref ? off(k + i, k + c) : kBufOOB);
-                    acc[s][e][cb][r] = re(x);
-                    if constexpr (CPLX) aci[s][e][cb][r] = x.im;
-                });
-            });
-        });
-    });
-    auto negate_all = [&]() __attribute__((always_inline)) {
+
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t ld;
+    int n, kp, RS, gw, l16, g;
+
+    __device__ __forceinline__ uint32_t off(int row, int col) const {
+        return UPPER ? (uint32_t(row) * ld + uint32_t(col)) * S : (uint32_t(col) * ld + uint32_t(row)) * S;
+    }
+    __device__ __forceinline__ void negate_all() {
         static_for<0, MAXS>([&](auto ss) {
             static_for<0, 2>([&](auto ee) {
                 static_for<0, 2>([&](auto cc) {
@@ -292,8 +285,37 @@ __device__ __forceinline__ void panel_gemm(__amdgpu_buffer_rsrc_t rs, uint32_t l
                 });
             });
         });
-    };
-    if (k > 0 && wave < RS) {   // waves without a superblock skip the loop
+    }
+    // accumulators from S(kp:n, kp:kp+w) (referenced part only): tile (s, e, cb),
+    // register r holds column c = 2 row(r, g) + cb, row i = 32 sb + 2 l16 + e
+    __device__ __forceinline__ void begin(int w) {
+        static_for<0, MAXS>([&](auto ss) {
+            constexpr int s = ss;
+            const int sb = gw + GW * s;
+            static_for<0, 2>([&](auto ee) {
+                static_for<0, 2>([&](auto cc) {
+                    static_for<0, 4>([&](auto rr) {
+                        constexpr int e = ee, cb = cc, r = rr;
+                        const int c = 2 * M::row(r, g) + cb;
+                        const int i = 32 * sb + 2 * l16 + e;
+                        const bool ref = sb < RS && kp + i < n && c < w && i >= c;
+                        const T x = buf_load<T>(rs, ref ? off(kp + i, kp + c) : kBufOOB);
+                        acc[s][e][cb][r] = re(x);
+                        if constexpr (CPLX) aci[s][e][cb][r] = x.im;
+                    });
+                });
+            });
+        });
+    }
+    // adds L(kp:n, q0:q1) L(kp:kp+w, q0:q1)^H (q0, q1 multiples of 4); FIRST:
+    // the accumulators still hold S (begin() just issued its loads) and are
+    // turned into -S once the first operand loads are in flight
+    template <bool FIRST>
+    __device__ __forceinline__ void accumulate(int q0, int q1) {
+        if (q1 <= q0 || gw >= RS) {   // nothing to add, or no superblock on this wave
+            if constexpr (FIRST) negate_all();
+            return;
+        }
         T opa[NS][2], opb[NS][MAXS][2];
         // A masked lane gets bit 31 set in its offset, which puts it out of the
         // buffer's range (no memory access, the load returns 0).  The mask is
@@ -322,11 +344,11 @@ __device__ __forceinline__ void panel_gemm(__amdgpu_buffer_rsrc_t rs, uint32_t l
         };
         auto load_ops = [&](int q, auto setc) __attribute__((always_inline)) {
             constexpr int st = decltype(setc)::value;
-            const bool live = q < k;
-            load_pair(k + 2 * l16, q + g, live, opa[st][0], opa[st][1]);
+            const bool live = q < q1;
+            load_pair(kp + 2 * l16, q + g, live, opa[st][0], opa[st][1]);
             static_for<0, MAXS>([&](auto ss) {
                 constexpr int s = ss;
-                const int row = k + 32 * (wave + WAVES * s) + 2 * l16;
+                const int row = kp + 32 * (gw + GW * s) + 2 * l16;
                 load_pair(row, q + g, live, opb[st][s][0], opb[st][s][1]);
             });
         };
@@ -334,7 +356,7 @@ __device__ __forceinline__ void panel_gemm(__amdgpu_buffer_rsrc_t rs, uint32_t l
             constexpr int st = decltype(setc)::value;
             static_for<0, MAXS>([&](auto ss) {
                 constexpr int s = ss;
-                if (wave + WAVES * s < RS) {
+                if (gw + GW * s < RS) {
                     static_for<0, 2>([&](auto ee) {
                         static_for<0, 2>([&](auto cc) {
                             constexpr int e = ee, cb = cc;
@@ -349,38 +371,200 @@ __device__ __forceinline__ void panel_gemm(__amdgpu_buffer_rsrc_t rs, uint32_t l
                 }
             });
         };
-        static_for<0, NS - 1>([&](auto ss) { load_ops(4 * ss, ss); });
-        // from here on the accumulators hold L L^H - S
-        negate_all();
-        for (int q = 0; q < k; q += 4 * NS) {
+        static_for<0, NS - 1>([&](auto ss) { load_ops(q0 + 4 * ss, ss); });
+        if constexpr (FIRST) negate_all();
+        for (int q = q0; q < q1; q += 4 * NS) {
             static_for<0, NS>([&](auto ss) {
                 constexpr int s = ss;
                 load_ops(q + 4 * (s + NS - 1), ic<(s + NS - 1) % NS>{});
                 step(ss);
             });
         }
-        negate_all();
     }
-    // the panel P goes to LDS
-    static_for<0, MAXS>([&](auto ss) {
-        constexpr int s = ss;
-        const int sb = wave + WAVES * s;
-        if (sb < RS) {
-            static_for<0, 2>([&](auto ee) {
-                static_for<0, 2>([&](auto cc) {
-                    static_for<0, 4>([&](auto rr) {
-                        constexpr int e = ee, cb = cc, r = rr;
-                        const int c = 2 * M::row(r, g) + cb;
-                        const int i = 32 * sb + 2 * l16 + e;
-                        T val;
-                        if constexpr (CPLX) val = T{acc[s][e][cb][r], UPPER ? -aci[s][e][cb][r] : aci[s][e][cb][r]};
-                        else val = acc[s][e][cb][r];
-                        pb[i * LDD + c] = c < w ? val : zero<T>();
+    // P = -(accumulators) into the panel buffer
+    __device__ __forceinline__ void finish(T* pb, int w) {
+        negate_all();
+        static_for<0, MAXS>([&](auto ss) {
+            constexpr int s = ss;
+            const int sb = gw + GW * s;
+            if (sb < RS) {
+                static_for<0, 2>([&](auto ee) {
+                    static_for<0, 2>([&](auto cc) {
+                        static_for<0, 4>([&](auto rr) {
+                            constexpr int e = ee, cb = cc, r = rr;
+                            const int c = 2 * M::row(r, g) + cb;
+                            const int i = 32 * sb + 2 * l16 + e;
+                            T val;
+                            if constexpr (CPLX) val = T{acc[s][e][cb][r], UPPER ? -aci[s][e][cb][r] : aci[s][e][cb][r]};
+                            else val = acc[s][e][cb][r];
+                            pb[i * LDD + c] = c < w ? val : zero<T>();
+                        });
                     });
                 });
-            });
+            }
+        });
+    }
+};
+
+// One matrix, panel by panel, with look-ahead: wave 0 factors the diagonal
+// block of panel k while the other GW = WAVES - 1 waves already run the GEMM
+// of panel k + 32 over the columns left of k (final since earlier panels);
+// after the solve of panel k they add its 32 columns and write the new panel:
+//
+//   GEMM(0) -> pb
+//   for k:  [wave 0: factor + invert pb's diagonal block | waves 1..: begin
+//            GEMM(k+32), add columns 0..k]  sync
+//           solve the rows below (all waves), L21 to memory  sync
+//           [waves 1..: add columns k..k+32, GEMM(k+32) -> pb]  sync
+template <typename T, bool UPPER, bool PAIRED>
+__device__ __forceinline__ void factor_matrix(__amdgpu_buffer_rsrc_t rs, uint32_t ld, int n,
+                                              int wave, T* pb, T* wm,
+                                              typename FactorType<T>::type* colx,
+                                              typename Traits<typename FactorType<T>::type>::R* rdiag,
+                                              int32_t* s_inf)
+{
+    using R = typename Traits<T>::R;
+    constexpr bool CPLX = Traits<T>::cplx;
+    using M = Mfma<R>;
+    using v4 = typename M::v4;
+    constexpr int GW = WAVES - 1;
+    constexpr int MAXT = Shape<T>::MAXT;
+    constexpr uint32_t S = sizeof(T);
+    auto off = [&](int row, int col) -> uint32_t {
+        return UPPER ? (uint32_t(row) * ld + uint32_t(col)) * S : (uint32_t(col) * ld + uint32_t(row)) * S;
+    };
+    // The lane index is re-read at every phase and hidden from the optimiser,
+    // so that addresses derived from it are recomputed where they are used
+    // instead of being hoisted and kept live (in registers) across phases.
+    auto lane_now = [&]() __attribute__((always_inline)) {
+        int lane = threadIdx.x & 63;
+        asm volatile("" : "+v"(lane));
+        return lane;
+    };
+    // ---- rows below the diagonal block of panel k: L21 = P21 W^H on MFMA,
+    // with P21 (rows) and conj(W) (columns) read from LDS
+    auto solve = [&](int k, int w) __attribute__((always_inline)) {
+        const int lane = lane_now();
+        const int l16 = lane & 15, g = lane >> 4;
+        const int RB = (n - k + 15) >> 4;         // 16-row blocks of the panel
+        static_for<0, MAXT>([&](auto tt) {
+            constexpr int t = tt;
+            const int ib = wave + WAVES * t;
+            if (ib >= 2 && ib < RB) {
+                static_for<0, 2>([&](auto pp) {
+                    constexpr int cbp = pp;
+                    v4 x = {R(0), R(0), R(0), R(0)};
+                    v4 xi = {R(0), R(0), R(0), R(0)};
+                    static_for<0, 4 * (cbp + 1)>([&](auto uu) {   // W is lower triangular
+                        constexpr int u = uu;
+                        const int c = 4 * u + g;                  // contraction index
+                        const T ao = pb[(ib * 16 + l16) * LDD + c];
+                        const T bo = wm[(cbp * 16 + l16) * LDD + c];
+                        if constexpr (CPLX) cmac<false>(ao.re, ao.im, bo.re, bo.im, x, xi);
+                        else x = M::mac(ao, bo, x);
+                    });
+                    static_for<0, 4>([&](auto rr) {
+                        constexpr int r = rr;
+                        const int row = k + ib * 16 + M::row(r, g);
+                        const int col = cbp * 16 + l16;
+                        const bool st = row < n && col < w;
+                        T val;
+                        if constexpr (CPLX) val = T{x[r], UPPER ? -xi[r] : xi[r]};
+                        else val = x[r];
+                        buf_store<T>(rs, st ? off(row, k + col) : kBufOOB, val);
+                    });
+                });
+            }
+        });
+    };
+    auto factor_block = [&](int k, int w) __attribute__((always_inline)) {
+        const int lane = lane_now();
+        if constexpr (CPLX) factor_invert_inplace<T, UPPER>(pb, wm, rdiag, lane, k, n, w, rs, ld, *s_inf);
+        else factor_invert<T, UPPER>(pb, wm, colx, rdiag, lane, k, n, w, rs, ld, *s_inf);
+    };
+    // cdouble: no look-ahead (its accumulators for 7 waves, the operand ring
+    // and the solve do not fit in the registers together); every wave takes
+    // part in each panel's GEMM, then wave 0 factors, then all solve.
+    if constexpr (CPLX && sizeof(R) == 8) {
+        using G = PanelGemm<T, UPPER, PAIRED, WAVES>;
+        G gm;
+        gm.rs = rs;
+        gm.ld = ld;
+        gm.n = n;
+        gm.gw = wave;
+        for (int k = 0; k < n; k += NBP) {
+            const int w = min(NBP, n - k);
+            const int lane = lane_now();
+            gm.l16 = lane & 15;
+            gm.g = lane >> 4;
+            gm.kp = k;
+            gm.RS = (n - k + 31) >> 5;
+            gm.begin(w);
+            gm.template accumulate<true>(0, k);
+            gm.finish(pb, w);
+            __syncthreads();
+            if (wave == 0) factor_block(k, w);
+            __syncthreads();
+            solve(k, w);
+            __syncthreads();
         }
-    });
+        return;
+    }
+    // The two roles run separate copies of the panel loop with the same
+    // barriers, so that the GEMM accumulators do not exist on wave 0's path
+    // (the factorisation there needs most of the registers).
+    if (wave == 0) {
+        __syncthreads();                          // GEMM of panel 0
+        for (int k = 0; k < n; k += NBP) {
+            const int w = min(NBP, n - k);
+            factor_block(k, w);
+            __syncthreads();
+            solve(k, w);
+            __syncthreads();   // the panel is in memory before the next GEMM reads it
+            if (k + NBP < n) __syncthreads();     // next panel's GEMM
+        }
+    } else {
+        using G = PanelGemm<T, UPPER, PAIRED, GW>;
+        G gm;
+        gm.rs = rs;
+        gm.ld = ld;
+        gm.n = n;
+        gm.gw = wave - 1;
+        auto set_panel = [&](int kp) __attribute__((always_inline)) {
+            const int lane = lane_now();
+            gm.l16 = lane & 15;
+            gm.g = lane >> 4;
+            gm.kp = kp;
+            gm.RS = (n - kp + 31) >> 5;
+        };
+        // ---- GEMM of panel 0: S(0:n, 0:32) alone
+        set_panel(0);
+        gm.begin(min(NBP, n));
+        gm.template accumulate<true>(0, 0);
+        gm.finish(pb, min(NBP, n));
+        __syncthreads();
+        for (int k = 0; k < n; k += NBP) {
+            const int w = min(NBP, n - k);
+            const int kn = k + NBP;
+            // the next panel's GEMM over the columns left of k (while wave 0
+            // factors the diagonal block of panel k)
+            if (kn < n) {
+                set_panel(kn);
+                gm.begin(min(NBP, n - kn));
+                gm.template accumulate<true>(0, k);
+            }
+            __syncthreads();
+            solve(k, w);
+            __syncthreads();
+            // add the columns of panel k, then P -> pb
+            if (kn < n) {
+                set_panel(kn);
+                gm.template accumulate<false>(k, kn);
+                gm.finish(pb, min(NBP, n - kn));
+                __syncthreads();
+            }
+        }
+    }
 }
 
 template <typename T, bool UPPER>
@@ -392,9 +576,7 @@ __global__ __launch_bounds__(64 * WAVES) void potrf_blocked_kernel(
     using C = typename FactorType<T>::type;
     using Rc = typename Traits<C>::R;
     constexpr bool CPLX = Traits<T>::cplx;
-    using M = Mfma<R>;
-    using v4 = typename M::v4;
-    constexpr int MAXN = Shape<T>::MAXN, MAXT = Shape<T>::MAXT;
+    constexpr int MAXN = Shape<T>::MAXN;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     T* pb = reinterpret_cast<T*>(smem);       // the panel P, MAXN rows x LDD
     T* wm = pb + MAXN * LDD;                  // conj of the inverse of the diagonal block's factor
@@ -403,85 +585,17 @@ __global__ __launch_bounds__(64 * WAVES) void potrf_blocked_kernel(
     int32_t* s_inf = reinterpret_cast<int32_t*>(rdiag + NBP);
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    constexpr uint32_t S = sizeof(T);
     const uint32_t ld = uint32_t(lda);
-    // byte offset of S(row, col) inside the matrix (the host guarantees < 2^31)
-    auto off = [&](int row, int col) -> uint32_t {
-        return UPPER ? (uint32_t(row) * ld + uint32_t(col)) * S : (uint32_t(col) * ld + uint32_t(row)) * S;
-    };
-
     for (int64_t b = blockIdx.x; b < batch; b += gridDim.x) {
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(A + b * stride);
         if (threadIdx.x == 0) *s_inf = 0;
-
-        for (int k = 0; k < n; k += NBP) {
-            // The lane index is re-read each panel and hidden from the
-            // optimiser, so addresses derived from it are recomputed per panel
-            // instead of being hoisted out of the loop, where they would stay
-            // live (in registers) across the diagonal-block factorisation.
-            int lane = threadIdx.x & 63;
-            asm volatile("" : "+v"(lane));
-            const int l16 = lane & 15, g = lane >> 4;
-            const int w = min(NBP, n - k);            // panel width
-            const int RB = (n - k + 15) >> 4;         // 16-row blocks of the panel (solve)
-            // ---- (i) the panel's GEMM; each wave owns the 32-row superblocks
-            // sb = wave + WAVES s of the panel, split into the even and the odd
-            // rows (two 16-row MFMA tiles), and the panel's 32 columns are split
-            // the same way (cb = 0: even columns, cb = 1: odd columns), so that a
-            // lane loads two consecutive rows of a column at once where the layout
-            // allows it (Lower with n even: one 16-byte load).
-            const int RS = (n - k + 31) >> 5;         // 32-row superblocks of the panel
-            // (the paired 16-byte loads are used for fp64 only: the fp32 pairs
-            // gave wrong results on the GPU and are not used)
-            if constexpr (!UPPER && !CPLX && sizeof(R) == 8) {
-                if ((n & 1) == 0) panel_gemm<T, UPPER, true>(rs, ld, n, k, w, RS, wave, l16, g, pb);
-                else panel_gemm<T, UPPER, false>(rs, ld, n, k, w, RS, wave, l16, g, pb);
-            } else {
-                panel_gemm<T, UPPER, false>(rs, ld, n, k, w, RS, wave, l16, g, pb);
-            }
-            __syncthreads();
-
-            // ---- (ii) factor and invert the diagonal block on wave 0
-            if (wave == 0) {
-                if constexpr (CPLX) factor_invert_inplace<T, UPPER>(pb, wm, rdiag, lane, k, n, w, rs, ld, *s_inf);
-                else factor_invert<T, UPPER>(pb, wm, colx, rdiag, lane, k, n, w, rs, ld, *s_inf);
-            }
-            __syncthreads();
-
-            // ---- (iii) rows below the diagonal block: L21 = P21 W^H on MFMA,
-            // with P21 (rows) and conj(W) (columns) read from LDS
-            asm volatile("" : "+v"(lane));   // (addresses of the solve are formed here)
-            const int l16s = lane & 15, gs = lane >> 4;
-            static_for<0, MAXT>([&](auto tt) {
-                constexpr int t = tt;
-                const int ib = wave + WAVES * t;
-                if (ib >= 2 && ib < RB) {
-                    static_for<0, 2>([&](auto pp) {
-                        constexpr int cbp = pp;
-                        v4 x = {R(0), R(0), R(0), R(0)};
-                        v4 xi = {R(0), R(0), R(0), R(0)};
-                        static_for<0, 4 * (cbp + 1)>([&](auto uu) {   // W is lower triangular
-                            constexpr int u = uu;
-                            const int c = 4 * u + gs;                  // contraction index
-                            const T ao = pb[(ib * 16 + l16s) * LDD + c];
-                            const T bo = wm[(cbp * 16 + l16s) * LDD + c];
-                            if constexpr (CPLX) cmac<false>(ao.re, ao.im, bo.re, bo.im, x, xi);
-                            else x = M::mac(ao, bo, x);
-                        });
-                        static_for<0, 4>([&](auto rr) {
-                            constexpr int r = rr;
-                            const int row = k + ib * 16 + M::row(r, gs);
-                            const int col = cbp * 16 + l16s;
-                            const bool st = row < n && col < w;
-                            T val;
-                            if constexpr (CPLX) val = T{x[r], UPPER ? -xi[r] : xi[r]};
-                            else val = x[r];
-                            buf_store<T>(rs, st ? off(row, k + col) : kBufOOB, val);
-                        });
-                    });
-                }
-            });
-            __syncthreads();   // the panel is in memory before the next GEMM reads it
+        // (the paired 16-byte loads are used for fp64 Lower with n even; the
+        // fp32 pairs gave wrong results on the GPU and are not used)
+        if constexpr (!UPPER && !CPLX && sizeof(R) == 8) {
+            if ((n & 1) == 0) factor_matrix<T, UPPER, true>(rs, ld, n, wave, pb, wm, colx, rdiag, s_inf);
+            else factor_matrix<T, UPPER, false>(rs, ld, n, wave, pb, wm, colx, rdiag, s_inf);
+        } else {
+            factor_matrix<T, UPPER, false>(rs, ld, n, wave, pb, wm, colx, rdiag, s_inf);
         }
         if (threadIdx.x == 0 && info != nullptr) info[b] = *s_inf;
         __syncthreads();
