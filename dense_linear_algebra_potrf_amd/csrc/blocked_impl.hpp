@@ -92,86 +92,117 @@ __device__ __forceinline__ void cmac(R ar, R ai, R br, R bi, V& cr, V& ci) {
     ci = M::mac(CONJ ? nai : ai, br, ci);
 }
 
-// The diagonal block of a panel (real types), factored in double and inverted
-// by one wavefront, in two phases.
-//
-// Factor: lane i (i = lane mod 32; the upper half of the wave repeats the lower
-// half and writes nothing) holds row i of the block.  At step j the pivot
-// column is published through LDS, d = S(j, j) is read back, and rows below j
-// take the Schur update of their entries right of column j with the
-// multiplier S(i, j) / d; column j is then scaled by 1/sqrt(d) (the diagonal
-// becomes sqrt(d)).  Rows at or beyond n are the identity.  The factor goes to
-// the matrix and back into the first 32 rows of the panel buffer, with
-// 1/L(j, j) beside it.
-//
-// Inverse: lane c forms column c of W = L11^-1 by forward substitution,
-//     W(m, c) = (delta(m, c) - sum_{p < m} L(m, p) W(p, c)) / L(m, m),
-// reading the rows of L11 from LDS; columns are independent, so this needs no
-// exchange between lanes.  W goes to wm (row-major), the merged info to s_inf.
-// Plain unrolled loops keep each lane's 32 values in registers.  Every LDS
-// store here is unconditional (the two halves of the wave hold identical data
-// and write identical values): stores under a lane condition split the code
-// into many small blocks, after which the compiler keeps hundreds of values
-// live and spills.
+// LDS pointers as 32-bit offsets (address space 3), and a read pointer whose
+// value the optimiser cannot know before dep is computed (the reads through it
+// stay after dep's computation).
+template <typename V> using lds_cptr = __attribute__((address_space(3))) const V*;
+template <typename V> __device__ __forceinline__ uint32_t lds_offset(const V* p) {
+    return uint32_t(uintptr_t((lds_cptr<V>)p));   // (an address-space cast)
+}
+template <typename V, typename D> __device__ __forceinline__ lds_cptr<V> lds_after(uint32_t off, D dep) {
+    asm volatile("" : "+v"(off) : "v"(dep));
+    return (lds_cptr<V>)uintptr_t(off);
+}
+
+// The diagonal block of a panel (real types), factored in double by one
+// wavefront.  Lane i (i = lane mod 32; the upper half of the wave repeats the
+// lower half) holds row i of the block.  At step j the Schur pivot d = S(j, j)
+// is read from the published column (a lane read into scalar registers was
+// tried: the scalar pressure made the kernel spill), rows below j take the
+// Schur update of their entries right of column j with
+// the multiplier S(i, j) / d, and column j is scaled by 1/sqrt(d) (the
+// diagonal becomes sqrt(d)).  Column j + 1 is updated first and published to
+// LDS at once, so the exchange overlaps the rest of the step's updates.  Rows
+// at or beyond n are the identity.  The factor goes to the matrix and to the
+// first rows of the panel buffer, 1/L(j, j) to rdiag, and the inverse W of
+// the factor (below) to wm for the solve of the rows below.  Every LDS store is unconditional (the two
+// halves of the wave write identical values): stores under a lane condition
+// split the code into many small blocks, after which the compiler keeps
+// hundreds of values live and spills.
 template <typename T, bool UPPER>
-__device__ __forceinline__ void factor_invert(T* pb, T* wm, typename FactorType<T>::type* colx,
-                                              typename Traits<typename FactorType<T>::type>::R* rdiag,
-                                              int lane, int k, int n, int w,
-                                              __amdgpu_buffer_rsrc_t rs, uint32_t ld, int32_t& s_inf)
+__device__ __forceinline__ void factor_diag(T* pb, T* wm, double* colx, double* rdiag,
+                                            int lane, int k, int n, int w,
+                                            __amdgpu_buffer_rsrc_t rs, uint32_t ld, int32_t& s_inf)
 {
-    using C = typename FactorType<T>::type;
-    using Rc = typename Traits<C>::R;
     constexpr uint32_t S = sizeof(T);
     const int i = lane & 31;
     const bool writer = lane < 32;
     const bool pad = k + i >= n;
-    C v[NBP];
-#pragma unroll
-    for (int c = 0; c < NBP; ++c) {
-        const C x = cvt<C>(pb[i * LDD + c]);
-        const C id = select(c == i, one<C>(), zero<C>());
-        v[c] = select(pad, id, x);
-    }
+    double v[NBP];
+    static_for<0, NBP>([&](auto cc) {
+        constexpr int c = cc;
+        // (the read is made opaque so that it stays unconditional: sunk into a
+        // branch under the select, it splits the code into small blocks and
+        // the kernel spills)
+        double x = double(pb[i * LDD + c]);
+        asm volatile("" : "+v"(x));
+        v[c] = pad ? ((c == i) ? 1.0 : 0.0) : x;
+    });
     int32_t inf = s_inf;
-#pragma unroll
-    for (int j = 0; j < NBP; ++j) {
-        C* col = colx + (j & 1) * NBP;
-        col[i] = v[j];      // both halves of the wave write the same value
-        wave_lds_sync();
-        const Rc d = re(col[j]);
-        if (j < w) inf = (inf == 0 && !(d > Rc(0))) ? (k + j + 1) : inf;
-        Rc sq, rsd;
+    double rsd_mine = 1.0;
+    colx[i] = v[0];
+    wave_lds_sync();
+    const uint32_t cxo = lds_offset(colx);
+    static_for<0, NBP>([&](auto jj) {
+        constexpr int j = jj;
+        // column j, published at step j - 1 (its reads stay in this step),
+        // read in one batch: consumed one by one, the reads would each wait
+        // for the previous one
+        const lds_cptr<double> col = lds_after<double>(cxo + uint32_t((j & 1) * NBP) * 8u, v[j]);
+        double cv[NBP];
+        static_for<j, NBP>([&](auto mm) { cv[mm] = col[mm]; });
+        __builtin_amdgcn_sched_barrier(0);
+        const double d = cv[j];
+        if (j < w) inf = (inf == 0 && !(d > 0.0)) ? (k + j + 1) : inf;
+        double sq, rsd;
         pivot_sqrt_rsq(d, sq, rsd);
-        const C beta = scale(v[j], rsd * rsd);      // S(i, j) / d
+        const double beta = v[j] * (rsd * rsd);       // S(i, j) / d
         // rows at or above j only touch slots right of the diagonal (unused)
-#pragma unroll
-        for (int m = j + 1; m < NBP; ++m) sub_mul_conj(v[m], beta, col[m]);
-        v[j] = select(i == j, diag_value<C>(sq, UPPER), scale(v[j], rsd));   // rows above j: unused slot
-        rdiag[j] = rsd;     // the same value in every lane
-    }
-    // the factor: to the matrix (conjugated for Upper), and into the panel
-    // buffer for the inverse
-#pragma unroll
-    for (int c = 0; c < NBP; ++c) {
+        if constexpr (j + 1 < NBP) {
+            v[j + 1] = __builtin_fma(-beta, cv[j + 1], v[j + 1]);
+            colx[((j + 1) & 1) * NBP + i] = v[j + 1];
+        }
+        static_for<j + 2, NBP>([&](auto mm) {
+            constexpr int m = mm;
+            v[m] = __builtin_fma(-beta, cv[m], v[m]);
+        });
+        v[j] = (i == j) ? sq : v[j] * rsd;            // rows above j: unused slot
+        rsd_mine = (i == j) ? rsd : rsd_mine;
+        wave_lds_sync();
+    });
+    // the factor: to the matrix, and into the first rows of the panel buffer
+    static_for<0, NBP>([&](auto cc) {
+        constexpr int c = cc;
         const bool st = writer && c <= i && c < w && !pad;
         const uint32_t o = UPPER ? (uint32_t(k + i) * ld + uint32_t(k + c)) * S
                                  : (uint32_t(k + c) * ld + uint32_t(k + i)) * S;
-        buf_store<T>(rs, st ? o : kBufOOB, cvt<T>(UPPER ? conj(v[c]) : v[c]));
-        pb[i * LDD + c] = (c <= i) ? cvt<T>(v[c]) : zero<T>();
-    }
+        buf_store<T>(rs, st ? o : kBufOOB, T(v[c]));
+        pb[i * LDD + c] = (c <= i) ? T(v[c]) : T(0);
+    });
+    rdiag[i] = rsd_mine;
     wave_lds_sync();
-    // column i of the inverse (from the stored factor, as the solve will use
-    // it); wm keeps conj(W) so that the solve is a plain product
-    C x[NBP];
-#pragma unroll
-    for (int m = 0; m < NBP; ++m) {
-        C acc = select(m == i, one<C>(), zero<C>());
-#pragma unroll
-        for (int p = 0; p < m; ++p) sub_mul(acc, cvt<C>(pb[m * LDD + p]), x[p]);
-        x[m] = scale(acc, rdiag[m]);
-    }
-#pragma unroll
-    for (int m = 0; m < NBP; ++m) wm[m * LDD + i] = cvt<T>(conj(x[m]));
+    // Inverse: lane i forms column i of W = L11^-1 by forward substitution,
+    //     W(m, i) = (delta(m, i) - sum_{p < m} L(m, p) W(p, i)) / L(m, m),
+    // from the stored factor (as the solve will use it); columns are
+    // independent, so no exchange between lanes is needed.  Row m of L11 is
+    // read in one batch, and the sum runs as four interleaved partial sums.
+    const uint32_t pbo = lds_offset(pb);
+    double x[NBP];
+    static_for<0, NBP>([&](auto mm) {
+        constexpr int m = mm;
+        const lds_cptr<T> row = lds_after<T>(pbo + uint32_t(m * LDD) * uint32_t(sizeof(T)), x[m > 0 ? m - 1 : 0]);
+        double lr[NBP];
+        static_for<0, m>([&](auto pp) { lr[pp] = double(row[pp]); });
+        const double rd = rdiag[m];
+        __builtin_amdgcn_sched_barrier(0);
+        double acc[4] = {(m == i) ? 1.0 : 0.0, 0.0, 0.0, 0.0};
+        static_for<0, m>([&](auto pp) {
+            constexpr int p = pp;
+            acc[p & 3] = __builtin_fma(-lr[p], x[p], acc[p & 3]);
+        });
+        x[m] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * rd;
+    });
+    static_for<0, NBP>([&](auto mm) { wm[mm * LDD + i] = T(x[mm]); });
     if (lane == 0) s_inf = inf;
 }
 
@@ -266,7 +297,7 @@ struct PanelGemm {
     static constexpr uint32_t S = sizeof(T);
     static constexpr int MAXS = cdiv(Shape<T>::MAXN / 32, GW);   // superblocks per wave
     // ring depth: as deep as 256 registers allow next to the accumulators
-    static constexpr int NS = 4;
+    static constexpr int NS = (!CPLX && sizeof(R) == 8) ? 3 : 4;
     v4 acc[MAXS][2][2], aci[MAXS][2][2];
 
     __amdgpu_buffer_rsrc_t rs;
@@ -477,10 +508,11 @@ __device__ __forceinline__ void factor_matrix(__amdgpu_buffer_rsrc_t rs, uint32_
             }
         });
     };
+
     auto factor_block = [&](int k, int w) __attribute__((always_inline)) {
         const int lane = lane_now();
         if constexpr (CPLX) factor_invert_inplace<T, UPPER>(pb, wm, rdiag, lane, k, n, w, rs, ld, *s_inf);
-        else factor_invert<T, UPPER>(pb, wm, colx, rdiag, lane, k, n, w, rs, ld, *s_inf);
+        else factor_diag<T, UPPER>(pb, wm, colx, rdiag, lane, k, n, w, rs, ld, *s_inf);
     };
     // cdouble: no look-ahead (its accumulators for 7 waves, the operand ring
     // and the solve do not fit in the registers together); every wave takes
@@ -567,6 +599,13 @@ __device__ __forceinline__ void factor_matrix(__amdgpu_buffer_rsrc_t rs, uint32_
     }
 }
 
+// LDS: the panel buffer, then wm (the inverse of the diagonal block's factor), then the
+// pivot exchange, 1 / L(j, j) and the info word
+template <typename T>
+constexpr int64_t aux_offset() { return int64_t(Shape<T>::MAXN) * LDD * sizeof(T); }
+template <typename T>
+constexpr int64_t aux_bytes() { return int64_t(NBP) * LDD * sizeof(T); }
+
 template <typename T, bool UPPER>
 __global__ __launch_bounds__(64 * WAVES) void potrf_blocked_kernel(
     T* __restrict__ A, int n, int64_t lda, int64_t stride, int64_t batch,
@@ -580,7 +619,7 @@ __global__ __launch_bounds__(64 * WAVES) void potrf_blocked_kernel(
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     T* pb = reinterpret_cast<T*>(smem);       // the panel P, MAXN rows x LDD
     T* wm = pb + MAXN * LDD;                  // conj of the inverse of the diagonal block's factor
-    C* colx = reinterpret_cast<C*>(wm + NBP * LDD);   // pivot exchange, 2 NBP
+    C* colx = reinterpret_cast<C*>(smem + aux_offset<T>() + aux_bytes<T>());   // pivot exchange, 2 NBP
     Rc* rdiag = reinterpret_cast<Rc*>(colx + 2 * NBP);   // 1 / L(j, j), NBP
     int32_t* s_inf = reinterpret_cast<int32_t*>(rdiag + NBP);
 
@@ -609,8 +648,7 @@ template <typename T>
 constexpr int64_t lds_bytes() {
     using C = typename FactorType<T>::type;
     using Rc = typename Traits<C>::R;
-    return int64_t(Shape<T>::MAXN * LDD + NBP * LDD) * sizeof(T) + 2 * NBP * sizeof(C) +
-           NBP * sizeof(Rc) + 16;
+    return aux_offset<T>() + aux_bytes<T>() + 2 * NBP * sizeof(C) + NBP * sizeof(Rc) + 16;
 }
 
 template <typename T>
