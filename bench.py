@@ -83,7 +83,7 @@ def make_input(cfg: dict):
     return abuf, bbuf
 
 
-def bench_config(name: str, steps: int, warmup: int) -> dict:
+def bench_config(name: str, steps: int, warmup: int, use_graph: bool = True) -> dict:
     import torch
     import dense_linear_algebra_potrf_amd as bl
     from dense_linear_algebra_potrf_amd import metrics
@@ -114,6 +114,19 @@ def bench_config(name: str, steps: int, warmup: int) -> dict:
 
     for k in range(warmup):
         launch(k)
+    torch.cuda.synchronize()
+    # The K timed calls are captured into one HIP graph (capture records the
+    # launches without running them) and replayed once: the kernels then run
+    # back to back, where a Python loop of short kernels would leave the GPU
+    # idle between launches.  Each call has its own input copy, so the single
+    # replay factors K fresh batches.
+    graph = None
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for k in range(steps):
+                launch(warmup + k)
+        torch.cuda.synchronize()
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     flush.fill_(7)
     del flush
@@ -121,17 +134,22 @@ def bench_config(name: str, steps: int, warmup: int) -> dict:
     # between launches would itself open a gap of several microseconds.  Every
     # family is a single launch per call, so the region's time over K is the
     # average duration of the dominant kernel.
+    stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for k in range(steps):
-        launch(warmup + k)
+    if graph is not None:
+        graph.replay()
+    else:
+        for k in range(steps):
+            launch(warmup + k)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms = [ev0.elapsed_time(ev1) / steps]
+    del graph
     # correctness guard on the last step: info must be as planted
     info_h = info.cpu().numpy()
     if cfg.get("plant"):
@@ -242,6 +260,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the timed calls from Python instead of one graph replay")
     a = ap.parse_args(argv)
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -260,7 +280,7 @@ def main(argv=None) -> int:
     import dense_linear_algebra_potrf_amd as bl
     bl.load_library()
 
-    prim = bench_config(a.config, a.steps, a.warmup)
+    prim = bench_config(a.config, a.steps, a.warmup, use_graph=not a.no_graph)
     attach_traffic(a.config, prim)
     cfg = CONFIGS[a.config]
     out = {
@@ -296,7 +316,8 @@ def main(argv=None) -> int:
             except bl.BatchlasError as e:
                 sec[name] = {"skipped": str(e)}
                 continue
-            r = bench_config(name, max(3, min(a.steps, 10)), max(1, min(a.warmup, 3)))
+            r = bench_config(name, max(3, min(a.steps, 10)), max(1, min(a.warmup, 3)),
+                             use_graph=not a.no_graph)
             attach_traffic(name, r)
             sec[name] = r
             print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step, {r['gbs']:.0f} GB/s, "

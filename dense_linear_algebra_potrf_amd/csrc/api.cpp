@@ -108,7 +108,7 @@ int auto_tiny_cut(DT dt) {
     switch (dt) {
     case DT::F32: return 33;
     case DT::F64: return 32;
-    case DT::C64: return 32;
+    case DT::C64: return 64;    // the 64 x 1 window beats the LDS family at 33..64
     case DT::C128: return 16;
     }
     return 0;

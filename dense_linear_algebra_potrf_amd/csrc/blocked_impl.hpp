@@ -38,6 +38,8 @@
 
 #include "families.hpp"
 
+#include <atomic>
+
 namespace bl {
 namespace blocked_detail {
 
@@ -668,6 +670,24 @@ bool geometry_t(int n, int64_t batch, Geometry& g) {
     return true;
 }
 
+// The dynamic LDS limit is raised once per kernel and device (the attribute
+// stays set; doing it at every call would also put a non-stream call inside
+// a caller's stream capture).  Concurrent first calls may both set it, which
+// is harmless.
+template <typename K>
+hipError_t allow_lds(K kernel, size_t shm) {
+    static std::atomic<uint32_t> done{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint32_t bit = dev < 32 ? (1u << dev) : 0u;
+    if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(shm));
+    if (e == hipSuccess) done.fetch_or(bit, std::memory_order_relaxed);
+    return e;
+}
+
 template <typename T>
 hipError_t potrf_t(bool upper, int n, void* A, int64_t lda, int64_t stride, int64_t batch,
                    int32_t* info, hipStream_t s) {
@@ -676,13 +696,11 @@ hipError_t potrf_t(bool upper, int n, void* A, int64_t lda, int64_t stride, int6
     T* a = static_cast<T*>(A);
     const size_t shm = size_t(lds_bytes<T>());
     if (upper) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(potrf_blocked_kernel<T, true>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(shm));
+        hipError_t e = allow_lds(potrf_blocked_kernel<T, true>, shm);
         if (e != hipSuccess) return e;
         return launch(potrf_blocked_kernel<T, true>, gd, bd, shm, s, a, n, lda, stride, batch, info);
     }
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(potrf_blocked_kernel<T, false>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(shm));
+    hipError_t e = allow_lds(potrf_blocked_kernel<T, false>, shm);
     if (e != hipSuccess) return e;
     return launch(potrf_blocked_kernel<T, false>, gd, bd, shm, s, a, n, lda, stride, batch, info);
 }

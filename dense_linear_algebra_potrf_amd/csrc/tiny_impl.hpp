@@ -146,6 +146,95 @@ __device__ __forceinline__ void tiny_solves(const T (&a)[R][P * R], const typena
     });
 }
 
+// The column recurrence on the rows a lane holds (rows i = q + r P of the
+// matrix of partition p), with the pivot columns exchanged through xbuf
+// (two parity buffers of PARTS rows of ROWW words).  On return a holds the
+// factor's rows, invd 1 / L(i, i) (posv only) and inf the first failing column.
+//
+// Register slots a[r][k] with k > i (the row's upper part) are scratch: they
+// absorb updates but never feed a referenced slot, so a step needs no
+// per-row guards.  Rows at or beyond n hold the identity, so every one of
+// the NB steps can run unconditionally: a padding step sees d = 1 and
+// leaves the referenced part alone.  After a failed pivot the recurrence
+// continues (NaN from the failing column on); the leading columns are final
+// by then and info keeps the first failing column.
+    //
+// Look-ahead: within step j, column j+1 is updated first and published to
+// LDS before the rest of step j's updates, so the exchange latency hides
+// behind that arithmetic.  Column j is published at slots relative to j
+// (row i -> slot i - j), so the entries a step needs always start at slot
+// 0; a step reads them from LDS where it uses them (broadcast reads), so no
+// copy of the column is held in registers.  Rows above j write to a spare
+// slot at NB.
+template <typename T, int P, int R, bool UPPER, int NRHS, int ROWW>
+__device__ __forceinline__ void factor_rows(T (&a)[R][P * R], typename Traits<T>::R (&invd)[R],
+                                            uint32_t* xbuf, int p, int q, int32_t& inf)
+{
+    using Rt = typename Traits<T>::R;
+    constexpr int NB = P * R;
+    constexpr int PARTS = 63 / P + 1;
+    auto xrow = [&](int par, int part) -> uint32_t* { return xbuf + (par * PARTS + part) * ROWW; };
+    auto publish = [&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int rj = j / P;
+        uint32_t* row = xrow(j & 1, p);
+        static_for<rj, R>([&](auto rr) {
+            constexpr int r = rr;
+            const int i = q + r * P;
+            const int slot = (r == rj) ? ((i >= j) ? i - j : NB) : i - j;
+            lds_put<T>(row, slot, a[r][j]);
+        });
+    };
+    // entry for row k of column j (k >= j), read from the published column
+    // (the buffer of column j is not overwritten before step j + 2)
+    auto colv = [&](int j, int k) -> T { return lds_get<T>(xrow(j & 1, p), k - j); };
+
+    inf = 0;
+    static_for<0, R>([&](auto rr) { invd[rr] = Rt(1); });
+    publish(ic<0>{});
+    wave_lds_sync();
+    static_for<0, NB>([&](auto jj) {
+        constexpr int j = jj;
+        constexpr int rj = j / P;
+        const Rt d = re(colv(j, j));
+        inf = (inf == 0 && !(d > Rt(0))) ? (j + 1) : inf;
+        const Rt inv = pivot_rcp(d);
+        const Rt rs = pivot_rsq(d);
+        T t[R];
+        static_for<rj, R>([&](auto rr) {
+            constexpr int r = rr;
+            t[r] = scale(a[r][j], inv);
+        });
+        if constexpr (j + 1 < NB) {
+            constexpr int rn = (j + 1) / P;
+            const T cj1 = colv(j, j + 1);
+            static_for<rn, R>([&](auto rr) {
+                constexpr int r = rr;
+                sub_mul_conj(a[r][j + 1], t[r], cj1);
+            });
+            publish(ic<j + 1>{});
+            wave_lds_sync();
+        }
+        static_for<rj, R>([&](auto rr) {
+            constexpr int r = rr;
+            constexpr int kend = cmin(NB, (r + 1) * P);
+            static_for<j + 2, kend>([&](auto kk) {
+                constexpr int k = kk;
+                sub_mul_conj(a[r][k], t[r], colv(j, k));
+            });
+            if constexpr (r == rj) {
+                // the one row block that holds row j itself
+                const bool diag = (q + r * P) == j;
+                a[r][j] = select(diag, diag_value<T>(pivot_sqrt(d), UPPER), scale(a[r][j], rs));
+                if constexpr (NRHS > 0) invd[r] = diag ? rs : invd[r];
+            } else {
+                a[r][j] = scale(a[r][j], rs);
+            }
+        });
+    });
+
+}
+
 // Packed path: each matrix's image in LDS starts at a multiple of IMGP
 // elements, IMGP >= n*n with IMGP = P (mod 32), so that the partitions of a
 // wave read from different LDS banks.
@@ -323,80 +412,9 @@ __global__ __launch_bounds__(PACKED ? 64 : 64 * kTinyWaves) void potrf_tiny_kern
     });
     if constexpr (PACKED) wave_lds_sync();   // the exchange buffer reuses the image
 
-    // Register slots a[r][k] with k > i (the row's upper part) are scratch: they
-    // absorb updates but never feed a referenced slot, so a step needs no
-    // per-row guards.  Rows at or beyond n hold the identity, so every one of
-    // the NB steps can run unconditionally: a padding step sees d = 1 and
-    // leaves the referenced part alone.  After a failed pivot the recurrence
-    // continues (NaN from the failing column on); the leading columns are final
-    // by then and info keeps the first failing column.
-    //
-    // Look-ahead: within step j, column j+1 is updated first and published to
-    // LDS before the rest of step j's updates, so the exchange latency hides
-    // behind that arithmetic.  Column j is published at slots relative to j
-    // (row i -> slot i - j), so the entries a step needs always start at slot
-    // 0; a step reads them from LDS where it uses them (broadcast reads), so no
-    // copy of the column is held in registers.  Rows above j write to a spare
-    // slot at NB.
-    auto publish = [&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        constexpr int rj = j / P;
-        uint32_t* row = xrow(j & 1, p);
-        static_for<rj, R>([&](auto rr) {
-            constexpr int r = rr;
-            const int i = q + r * P;
-            const int slot = (r == rj) ? ((i >= j) ? i - j : NB) : i - j;
-            lds_put<T>(row, slot, a[r][j]);
-        });
-    };
-    // entry for row k of column j (k >= j), read from the published column
-    // (the buffer of column j is not overwritten before step j + 2)
-    auto colv = [&](int j, int k) -> T { return lds_get<T>(xrow(j & 1, p), k - j); };
-
     int32_t inf = 0;
     Rt invd[R];                 // 1 / L(i, i) of each held row (used by the solves)
-    static_for<0, R>([&](auto rr) { invd[rr] = Rt(1); });
-    publish(ic<0>{});
-    wave_lds_sync();
-    static_for<0, NB>([&](auto jj) {
-        constexpr int j = jj;
-        constexpr int rj = j / P;
-        const Rt d = re(colv(j, j));
-        inf = (inf == 0 && !(d > Rt(0))) ? (j + 1) : inf;
-        const Rt inv = pivot_rcp(d);
-        const Rt rs = pivot_rsq(d);
-        T t[R];
-        static_for<rj, R>([&](auto rr) {
-            constexpr int r = rr;
-            t[r] = scale(a[r][j], inv);
-        });
-        if constexpr (j + 1 < NB) {
-            constexpr int rn = (j + 1) / P;
-            const T cj1 = colv(j, j + 1);
-            static_for<rn, R>([&](auto rr) {
-                constexpr int r = rr;
-                sub_mul_conj(a[r][j + 1], t[r], cj1);
-            });
-            publish(ic<j + 1>{});
-            wave_lds_sync();
-        }
-        static_for<rj, R>([&](auto rr) {
-            constexpr int r = rr;
-            constexpr int kend = cmin(NB, (r + 1) * P);
-            static_for<j + 2, kend>([&](auto kk) {
-                constexpr int k = kk;
-                sub_mul_conj(a[r][k], t[r], colv(j, k));
-            });
-            if constexpr (r == rj) {
-                // the one row block that holds row j itself
-                const bool diag = (q + r * P) == j;
-                a[r][j] = select(diag, diag_value<T>(pivot_sqrt(d), UPPER), scale(a[r][j], rs));
-                if constexpr (NRHS > 0) invd[r] = diag ? rs : invd[r];
-            } else {
-                a[r][j] = scale(a[r][j], rs);
-            }
-        });
-    });
+    factor_rows<T, P, R, UPPER, NRHS, ROWW>(a, invd, xbuf, p, q, inf);
 
     if constexpr (NRHS > 0)
         tiny_solves<T, P, R, NRHS>(a, invd, xbuf, PARTS * ROWW, ROWW, p, q, live, n,
@@ -446,15 +464,17 @@ template <typename... Cs> struct TList {};
 
 // Ordered by order served (NB); the first entry with NB >= n is used.
 template <typename T> struct TinyConfigs;
+// (64 x 1: one matrix per wavefront, a lane per row, for orders 34..64; it
+// needs more than 256 registers, so one wavefront per SIMD)
 template <> struct TinyConfigs<float> {
     using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<17, 1>, TC<9, 2>, TC<8, 3>,
-                       TC<16, 2>, TC<11, 3>>;
+                       TC<16, 2>, TC<11, 3>, TC<64, 1>>;
 };
 template <> struct TinyConfigs<double> {
     using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<8, 3>, TC<8, 4>>;
 };
 template <> struct TinyConfigs<cfloat> {
-    using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<8, 3>, TC<8, 4>>;
+    using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<8, 3>, TC<8, 4>, TC<64, 1>>;
 };
 template <> struct TinyConfigs<cdouble> {
     using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>>;
@@ -463,6 +483,13 @@ template <> struct TinyConfigs<cdouble> {
 // posv keeps more per lane (both solves' right-hand sides): smaller windows for
 // the double types so that nothing spills.
 template <typename T> struct PosvConfigs { using type = typename TinyConfigs<T>::type; };
+template <> struct PosvConfigs<float> {
+    using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<17, 1>, TC<9, 2>, TC<8, 3>,
+                       TC<16, 2>, TC<11, 3>>;
+};
+template <> struct PosvConfigs<cfloat> {
+    using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<8, 3>, TC<8, 4>>;
+};
 template <> struct PosvConfigs<double> {
     using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<8, 3>>;
 };

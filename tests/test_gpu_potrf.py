@@ -57,7 +57,7 @@ def test_tiny_every_order(dt, uplo):
 @pytest.mark.parametrize("dt", DTS)
 @pytest.mark.parametrize("uplo", UPLOS)
 def test_tiny_poison_and_padding(dt, uplo):
-    for n in (1, 5, 8, 13, 16):
+    for n in (1, 5, 8, 13, 16, 33, 40, 64):
         if not runnable("tiny", dt, n, uplo):
             continue
         a = syn.spd_matrices(n, 77, dt, seed=n)
@@ -108,6 +108,12 @@ def test_config_cfloat_upper_n64_b16384(planted):
     a = syn.spd_matrices(64, 16384, "c64", seed=1004)
     want = syn.plant_failures(a, seed=1004, every=64) if planted else np.zeros(16384, np.int32)
     check_potrf(a, "U", expect_info=want, label="config c64 U n=64 b16384")
+
+
+def test_config_cfloat_upper_n64_b16384_lds_route():
+    a = syn.spd_matrices(64, 16384, "c64", seed=1004)
+    want = syn.plant_failures(a, seed=1004, every=64)
+    check_potrf(a, "U", family="lds", expect_info=want, label="config c64 U n=64 via lds")
 
 
 def test_config_fp32_n33_b16384_lds_route():
