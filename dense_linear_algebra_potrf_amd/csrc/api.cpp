@@ -313,9 +313,8 @@ batchlas_status do_posv(int family, int dt_, int uplo, int64_t n, int64_t nrhs, 
         return hip_status(bl::posv_tiny(dt, upper, int(n), int(nrhs), A, lda, strideA, B, ldb,
                                         strideB, batch, info, s),
                           "posv launch");
-    // split route: potrf (info is needed by the solve kernel to skip failed items)
-    if (info == nullptr)
-        return fail(BATCHLAS_NOT_SUPPORTED, "the split posv route needs an info array");
+    // split route: potrf, then both solves in one launch (failed items keep B;
+    // with info NULL the solve reads the failure off the factor's diagonal)
     st = do_potrf(bl::FAM_AUTO, dt_, uplo, n, A, lda, strideA, batch, info, stream);
     if (st != BATCHLAS_OK) return st;
     return hip_status(bl::potrs(dt, upper, int(n), int(nrhs), A, lda, strideA, B, ldb, strideB,

@@ -59,7 +59,6 @@ hipError_t blocked_potrf(DT dt, bool upper, int n, void* A, int64_t lda, int64_t
                          int64_t batch, int32_t* info, hipStream_t s);
 
 // --- the two triangular solves with an already factored A (posv split route)
-int potrs_max_nrhs();
 bool potrs_supported(DT dt, int n, int nrhs);
 hipError_t potrs(DT dt, bool upper, int n, int nrhs, const void* A, int64_t lda,
                  int64_t strideA, void* B, int64_t ldb, int64_t strideB, int64_t batch,

@@ -122,6 +122,10 @@ batchlas_status batchlas_potrf(batchlas_dtype dt, batchlas_uplo uplo, int64_t n,
  *   B          device pointer, n x nrhs per item, column-major
  *   ldb        >= n;  strideB >= ldb * nrhs
  * Other arguments as for batchlas_potrf.  A is overwritten with the factor.
+ * Small orders with nrhs <= 4 run fused in one kernel (POSV_TINY); every
+ * other shape that potrf serves runs as potrf followed by one kernel for both
+ * triangular solves (POSV_SPLIT), which also keeps B of failed items when
+ * info is NULL (it reads the failure off the factor's diagonal).
  */
 batchlas_status batchlas_posv(batchlas_dtype dt, batchlas_uplo uplo, int64_t n, int64_t nrhs,
                               void *A, int64_t lda, int64_t strideA,

@@ -72,3 +72,65 @@ def test_config_posv_fp32_n32_nrhs4_planted():
     b = syn.rhs(32, 4, 16384, "f32", seed=1003)
     _, _, info = check_posv(a, b, "L", label="config posv planted")
     assert (info > 0).sum() == 256
+
+
+# ---------------------------------------------------------------- split route
+# potrf by the dispatcher's family, then both triangular solves in one launch:
+# posv for orders and right-hand-side counts beyond the fused window.
+SPLIT_CASES = [(1, 1), (5, 6), (17, 3), (32, 5), (33, 4), (64, 9), (100, 2), (129, 5), (257, 3),
+               (512, 1)]
+
+
+def split_runnable(dt, n, nrhs):
+    import dense_linear_algebra_potrf_amd as bl
+    try:
+        bl.route(dt, "L", n, 8, nrhs=nrhs, family="posv_split")
+        return True
+    except bl.BatchlasError:
+        return False
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("uplo", ["L", "U"])
+def test_posv_split_orders(dt, uplo):
+    for n, nrhs in SPLIT_CASES:
+        if not split_runnable(dt, n, nrhs):
+            assert dt == "c128" and n > 256
+            continue
+        batch = 9 if n > 128 else 41
+        a = syn.spd_matrices(n, batch, dt, seed=50 * n + nrhs + (uplo == "U"))
+        syn.plant_failures(a, seed=n, every=4)
+        b = syn.rhs(n, nrhs, batch, dt, seed=n + 1)
+        check_posv(a, b, uplo, family="posv_split", label="split")
+
+
+@pytest.mark.parametrize("dt", ["f32", "c128"])
+def test_posv_split_padded_layout(dt):
+    for n, nrhs in ((40, 5), (7, 11)):
+        a = syn.spd_matrices(n, 23, dt, seed=n)
+        syn.plant_failures(a, seed=n, every=3)
+        b = syn.rhs(n, nrhs, 23, dt, seed=n)
+        check_posv(a, b, "L", family="posv_split", padded=True, label="split padded")
+
+
+@pytest.mark.parametrize("dt", ["f32", "c64"])
+def test_posv_split_without_info_matches(dt):
+    """info NULL: the solve reads failures off the factor's diagonal; X and the
+    factor must equal the run with info, bit for bit."""
+    import torch
+    import dense_linear_algebra_potrf_amd as bl
+    n, nrhs, batch = 45, 6, 64
+    a = syn.spd_matrices(n, batch, dt, seed=77)
+    syn.plant_failures(a, seed=77, every=5)
+    b = syn.rhs(n, nrhs, batch, dt, seed=78)
+    abuf, bbuf = syn.to_colmajor(a), syn.to_colmajor(b)
+    outs = []
+    for with_info in (True, False):
+        ta = torch.from_numpy(abuf.copy()).cuda()
+        tb = torch.from_numpy(bbuf.copy()).cuda()
+        bl.posv(ta, tb, "L", None if with_info else False, n=n, nrhs=nrhs, batch=batch,
+                family="posv_split")
+        torch.cuda.synchronize()
+        outs.append((ta.cpu().numpy(), tb.cpu().numpy()))
+    assert np.array_equal(outs[0][0].view(np.uint8), outs[1][0].view(np.uint8))
+    assert np.array_equal(outs[0][1].view(np.uint8), outs[1][1].view(np.uint8))
