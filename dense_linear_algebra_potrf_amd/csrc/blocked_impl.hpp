@@ -290,16 +290,16 @@ __device__ __forceinline__ void factor_invert_inplace(T* pb, T* wm, typename Tra
 // complex types keep the imaginary parts in aci; for Upper their arithmetic
 // runs on the stored values, conj(S) and conj(L), which gives conj(P), and the
 // conjugate is taken when P is written out.
-template <typename T, bool UPPER, bool PAIRED, int GW>
+template <typename T, bool UPPER, bool PAIRED, int GW, int MAXS_ = cdiv(Shape<T>::MAXN / 32, GW)>
 struct PanelGemm {
     using R = typename Traits<T>::R;
     static constexpr bool CPLX = Traits<T>::cplx;
     using M = Mfma<R>;
     using v4 = typename M::v4;
     static constexpr uint32_t S = sizeof(T);
-    static constexpr int MAXS = cdiv(Shape<T>::MAXN / 32, GW);   // superblocks per wave
+    static constexpr int MAXS = MAXS_;   // superblocks per wave (the caller keeps RS <= GW MAXS)
     // ring depth: as deep as 256 registers allow next to the accumulators
-    static constexpr int NS = (!CPLX && sizeof(R) == 8) ? 3 : 4;
+    static constexpr int NS = MAXS <= 2 ? (CPLX ? 4 : (sizeof(R) == 8 ? 5 : 6)) : (!CPLX && sizeof(R) == 8 ? 3 : 4);
     v4 acc[MAXS][2][2], aci[MAXS][2][2];
 
     __amdgpu_buffer_rsrc_t rs;
@@ -546,19 +546,42 @@ __device__ __forceinline__ void factor_matrix(__amdgpu_buffer_rsrc_t rs, uint32_
     }
     // The two roles run separate copies of the panel loop with the same
     // barriers, so that the GEMM accumulators do not exist on wave 0's path
-    // (the factorisation there needs most of the registers).
+    // across the factorisation (which needs most of the registers).  The
+    // GEMM waves hold at most two superblocks each: the GEMMs of panels 0 and
+    // 32 (16 and 15 superblocks, and nothing to overlap with) run on all eight
+    // waves; from panel 64 on at most 14 superblocks remain for seven waves.
+    auto gemm_all = [&](int kp) __attribute__((always_inline)) {
+        using G8 = PanelGemm<T, UPPER, PAIRED, WAVES, 2>;
+        G8 g8;
+        const int lane = lane_now();
+        g8.rs = rs;
+        g8.ld = ld;
+        g8.n = n;
+        g8.gw = wave;
+        g8.l16 = lane & 15;
+        g8.g = lane >> 4;
+        g8.kp = kp;
+        g8.RS = (n - kp + 31) >> 5;
+        g8.begin(min(NBP, n - kp));
+        g8.template accumulate<true>(0, kp);
+        g8.finish(pb, min(NBP, n - kp));
+    };
     if (wave == 0) {
-        __syncthreads();                          // GEMM of panel 0
+        gemm_all(0);
+        __syncthreads();
         for (int k = 0; k < n; k += NBP) {
             const int w = min(NBP, n - k);
             factor_block(k, w);
             __syncthreads();
             solve(k, w);
             __syncthreads();   // the panel is in memory before the next GEMM reads it
-            if (k + NBP < n) __syncthreads();     // next panel's GEMM
+            if (k + NBP < n) {
+                if (k == 0) gemm_all(NBP);
+                __syncthreads();     // next panel's GEMM
+            }
         }
     } else {
-        using G = PanelGemm<T, UPPER, PAIRED, GW>;
+        using G = PanelGemm<T, UPPER, PAIRED, GW, 2>;
         G gm;
         gm.rs = rs;
         gm.ld = ld;
@@ -571,18 +594,14 @@ __device__ __forceinline__ void factor_matrix(__amdgpu_buffer_rsrc_t rs, uint32_
             gm.kp = kp;
             gm.RS = (n - kp + 31) >> 5;
         };
-        // ---- GEMM of panel 0: S(0:n, 0:32) alone
-        set_panel(0);
-        gm.begin(min(NBP, n));
-        gm.template accumulate<true>(0, 0);
-        gm.finish(pb, min(NBP, n));
+        gemm_all(0);
         __syncthreads();
         for (int k = 0; k < n; k += NBP) {
             const int w = min(NBP, n - k);
             const int kn = k + NBP;
             // the next panel's GEMM over the columns left of k (while wave 0
             // factors the diagonal block of panel k)
-            if (kn < n) {
+            if (kn < n && k > 0) {
                 set_panel(kn);
                 gm.begin(min(NBP, n - kn));
                 gm.template accumulate<true>(0, k);
@@ -592,9 +611,13 @@ __device__ __forceinline__ void factor_matrix(__amdgpu_buffer_rsrc_t rs, uint32_
             __syncthreads();
             // add the columns of panel k, then P -> pb
             if (kn < n) {
-                set_panel(kn);
-                gm.template accumulate<false>(k, kn);
-                gm.finish(pb, min(NBP, n - kn));
+                if (k == 0) {
+                    gemm_all(kn);
+                } else {
+                    set_panel(kn);
+                    gm.template accumulate<false>(k, kn);
+                    gm.finish(pb, min(NBP, n - kn));
+                }
                 __syncthreads();
             }
         }
