@@ -276,7 +276,8 @@ constexpr int kPackedUpperMaxBytes = 12 * 1024;
 template <typename T, int P, int R, bool UPPER, int NRHS, bool PACKED>
 __global__ __launch_bounds__(PACKED ? 64 : 64 * kTinyWaves) void potrf_tiny_kernel(
     T* __restrict__ A, int n_arg, int64_t lda, int64_t stride, int64_t batch,
-    int32_t* __restrict__ info, T* __restrict__ B, int nrhs, int64_t ldb, int64_t strideB)
+    int32_t* __restrict__ info, T* __restrict__ B, int nrhs, int64_t ldb, int64_t strideB,
+    int gu)
 {
     const int n = PACKED ? P * R : n_arg;
     using Rt = typename Traits<T>::R;
@@ -295,9 +296,10 @@ __global__ __launch_bounds__(PACKED ? 64 : 64 * kTinyWaves) void potrf_tiny_kern
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int p = lane / P;
     const int q = lane - p * P;
-    const int64_t b_first = ((int64_t)blockIdx.x * WAVES + wave) * G;   // wave-uniform
+    const int GU = PACKED ? G : gu;       // matrices this wavefront takes (<= G; the rest idle)
+    const int64_t b_first = ((int64_t)blockIdx.x * WAVES + wave) * GU;   // wave-uniform
     const int64_t b = b_first + p;
-    const bool live = (p < G) && (b < batch);
+    const bool live = (p < GU) && (b < batch);
     uint32_t* const xbuf = &lds_raw[wave][0];
     auto xrow = [&](int par, int part) -> uint32_t* { return xbuf + (par * PARTS + part) * ROWW; };
     // One buffer descriptor per wavefront; the host guarantees every byte offset
@@ -457,8 +459,11 @@ __global__ __launch_bounds__(PACKED ? 64 : 64 * kTinyWaves) void potrf_tiny_kern
 }
 
 // ---------------------------------------------------------------- configurations
-template <int P_, int R_> struct TC {
-    static constexpr int P = P_, R = R_, NB = P_ * R_;
+// P lanes x R rows per matrix; GU matrices per wavefront (at most 64 / P:
+// fewer where measured faster, e.g. n = 33 takes 4 per wavefront, not 5).
+template <int P_, int R_, int GU_ = 64 / P_> struct TC {
+    static constexpr int P = P_, R = R_, NB = P_ * R_, GU = GU_;
+    static_assert(GU_ >= 1 && GU_ <= 64 / P_, "matrices per wavefront");
 };
 template <typename... Cs> struct TList {};
 
@@ -468,7 +473,7 @@ template <typename T> struct TinyConfigs;
 // needs more than 256 registers, so one wavefront per SIMD)
 template <> struct TinyConfigs<float> {
     using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<17, 1>, TC<9, 2>, TC<8, 3>,
-                       TC<16, 2>, TC<11, 3>, TC<64, 1>>;
+                       TC<16, 2>, TC<11, 3, 4>, TC<64, 1>>;
 };
 template <> struct TinyConfigs<double> {
     using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<8, 3>, TC<8, 4>>;
@@ -554,10 +559,11 @@ bool geometry_t(bool upper, int n, int64_t lda, int64_t stride, int64_t batch, G
         g.family = FAM_TINY;
         g.P = C::P;
         g.R = C::R;
-        g.G = G;
+        const int gw = packed ? G : C::GU;      // matrices per wavefront
+        g.G = gw;
         g.threads = 64 * waves;
         g.panel = 0;
-        g.grid = (batch + G * waves - 1) / (G * waves);
+        g.grid = (batch + gw * waves - 1) / (gw * waves);
         g.lds = packed ? 4 * (xw > iw ? xw : iw) : int64_t(waves) * xw * 4;
     });
 }
@@ -572,12 +578,13 @@ hipError_t launch_tiny(int n, T* a, int64_t lda, int64_t stride, int64_t batch, 
         if (packed_layout<C>(n, lda, stride)) {
             const int64_t grid = (batch + G - 1) / G;
             return launch(potrf_tiny_kernel<T, C::P, C::R, UPPER, NRHS, true>, dim3((unsigned)grid),
-                          dim3(64), 0, s, a, n, lda, stride, batch, info, b, nrhs, ldb, strideB);
+                          dim3(64), 0, s, a, n, lda, stride, batch, info, b, nrhs, ldb, strideB, G);
         }
     }
-    const int64_t grid = (batch + G * kTinyWaves - 1) / (G * kTinyWaves);
+    constexpr int gu = C::GU;
+    const int64_t grid = (batch + gu * kTinyWaves - 1) / (gu * kTinyWaves);
     return launch(potrf_tiny_kernel<T, C::P, C::R, UPPER, NRHS, false>, dim3((unsigned)grid),
-                  dim3(64 * kTinyWaves), 0, s, a, n, lda, stride, batch, info, b, nrhs, ldb, strideB);
+                  dim3(64 * kTinyWaves), 0, s, a, n, lda, stride, batch, info, b, nrhs, ldb, strideB, gu);
 }
 
 template <typename T>

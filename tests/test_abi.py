@@ -107,7 +107,8 @@ def test_route_tiny_geometry_invariants(lib):
                 assert e.status_name == "NOT_SUPPORTED"
                 continue
             P, R, G = r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]
-            assert P * R >= n and G == 64 // P and G >= 1
+            # up to 64 // P matrices per wavefront (fewer where measured faster)
+            assert P * R >= n and 1 <= G <= 64 // P
             assert r["grid"] * G * (r["block_threads"] // 64) >= 1000
             assert r["family"] == "tiny"
 
