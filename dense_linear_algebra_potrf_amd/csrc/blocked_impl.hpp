@@ -5,32 +5,29 @@
 // panel factorisation, a triangular solve of the panel below its diagonal
 // block, and a symmetric rank-k update that carries most of the flops).  The
 // pages run these as separate batched launches per panel; on CDNA4 one
-// workgroup keeps a whole matrix and runs the panels itself, left-looking, so
-// the trailing data never makes a round trip through HBM between launches:
+// workgroup of four wavefronts runs the panels of one matrix itself,
+// left-looking:
 //
 //   for each panel of NBP = 32 columns starting at k:
 //     (i)   GEMM: P = S(k:n, k:k+32) - L(k:n, 0:k) L(k:k+32, 0:k)^T on MFMA
 //           (v_mfma_*_16x16x4, accumulated as L L^T - S so that no operand needs
-//           negating), the 32-row superblocks spread over 7 waves; P goes to
-//           LDS (up to 512 x 33 elements);
-//     (ii)  the 32 x 32 diagonal block of P is factored on wave 0, and the
-//           inverse W of its factor is formed column by column, info merged
-//           as k + j + 1;
+//           negating).  Wave 0 computes the 32 x 32 diagonal block into LDS,
+//           the other waves the 32-row superblocks below it, in registers;
+//     (ii)  meanwhile wave 0 factors the diagonal block and forms the inverse
+//           W of its factor column by column, info merged as k + j + 1;
 //     (iii) the rows below are solved by a second MFMA product
-//           L21 = P21 W^T (W lower triangular, zero blocks skipped), both
-//           operands read from LDS, and written to the matrix, where the next
-//           panels read them.
-//   Look-ahead: while wave 0 works on (ii) for panel k, the other 7 waves
-//   already run (i) for panel k + 32 over the columns left of k, which are
-//   final; after (iii) they add the 32 columns of panel k.  So the one-wave
-//   diagonal phase overlaps the bulk of the next GEMM.
+//           L21 = P21 W^T (W lower triangular, zero blocks skipped) straight
+//           from the GEMM's accumulators, and L21 is written over S, where
+//           the next panels read it.
+//   Only the diagonal block, W and a few vectors live in LDS, so two
+//   workgroups (matrices) share a compute unit: while one factors its
+//   diagonal block on one wave, the other keeps the matrix cores busy.
 //
 // S = A for Lower, S(i, c) = conj(A(c, i)) for Upper; for the real types the
 // Upper form only swaps the address of each element.  The complex types run
 // the same schedule with each complex product split into four real MFMAs on
 // separate real and imaginary accumulators (the pages' complex trailing update
-// is a ConjTrans GEMM); cdouble is limited to order 256, where its panel
-// buffer still fits in LDS.  Only the referenced
+// is a ConjTrans GEMM).  Only the referenced
 // triangle is read or written; rows beyond n load as zero and are never
 // stored.  Failure handling follows the pages' info contract: the first
 // failing pivot column is kept; later work runs on with NaN.
@@ -38,22 +35,17 @@
 
 #include "families.hpp"
 
-#include <atomic>
-
 namespace bl {
 namespace blocked_detail {
 
 constexpr int NBP = 32;          // panel width
-constexpr int WAVES = 8;         // wavefronts per workgroup
+constexpr int WAVES = 4;         // wavefronts per workgroup
 constexpr int LDD = NBP + 1;     // padded row length of the LDS blocks
 
-// Largest order served (the panel buffer, MAXN x LDD elements, lives in LDS),
-// 32-row superblocks per wave in the GEMM and 16-row blocks per wave in the
-// solve.
+// Largest order served (the loops are not bounded by it; it is the range the
+// family is built and tested for).
 template <typename T> struct Shape {
-    static constexpr int MAXN = sizeof(T) == 16 ? 256 : 512;
-    static constexpr int MAXS = MAXN / 32 / WAVES;
-    static constexpr int MAXT = MAXN / 16 / WAVES;
+    static constexpr int MAXN = 512;
 };
 // The diagonal block is factored in double for the real types and in the
 // element type itself for the complex ones.
@@ -271,15 +263,14 @@ __device__ __forceinline__ void factor_invert_inplace(T* pb, T* wm, typename Tra
 // The GEMM of one panel starting at column kp:
 //     P = S(kp:n, kp:kp+w) - L(kp:n, 0:kp) L(kp:kp+w, 0:kp)^H,
 // accumulated on MFMA as L L^H - S (so that no operand needs negating) and
-// written, negated back, into the panel buffer pb (row i of the panel at
-// pb[i * LDD]; columns at or beyond w as 0).  The contraction can be split:
-// accumulate() adds the columns [q0, q1) of L, so that the part over columns
-// that are already final can run before the previous panel is solved.
+// written, negated back, over S in the matrix, except the diagonal block,
+// which goes to LDS for the factorisation (row i at p11[i * LDD]; columns at
+// or beyond w as 0).  accumulate() adds the columns [q0, q1) of L.
 //
-// The GW GEMM waves (gw = 0 .. GW-1) own the 32-row superblocks sb = gw + GW s
-// of the panel, each split into its even and odd rows (two 16-row MFMA tiles);
-// the panel's 32 columns are split the same way (cb = 0: even columns, cb = 1:
-// odd columns), so that a lane loads two consecutive rows of a column at once
+// A wave owns the 32-row superblocks sb = sb0 + GW s (s < MAXS) of the panel,
+// each split into its even and odd rows (two 16-row MFMA tiles); the panel's
+// 32 columns are split the same way (cb = 0: even columns, cb = 1: odd
+// columns), so that a lane loads two consecutive rows of a column at once
 // where the layout allows it.  MFMA roles: the A operand runs over the panel's
 // columns c (rows kp + c of L), the B operand over the panel's rows i; the
 // result is P^T tile by tile.  With PAIRED (fp64 Lower, n even), a lane loads
@@ -288,23 +279,26 @@ __device__ __forceinline__ void factor_invert_inplace(T* pb, T* wm, typename Tra
 // out-of-range offset (rows at or beyond n, steps past q1).  Operands live in
 // a ring of NS register sets, loads NS - 1 steps ahead of the MFMAs.  The
 // complex types keep the imaginary parts in aci; for Upper their arithmetic
-// runs on the stored values, conj(S) and conj(L), which gives conj(P), and the
-// conjugate is taken when P is written out.
-template <typename T, bool UPPER, bool PAIRED, int GW, int MAXS_ = cdiv(Shape<T>::MAXN / 32, GW)>
+// runs on the stored values, conj(S) and conj(L), which gives conj(P): the
+// stored form of P, as it is written back to the matrix; the block for LDS is
+// conjugated.
+template <typename T, bool UPPER, bool PAIRED, int GW, int MAXS_>
 struct PanelGemm {
     using R = typename Traits<T>::R;
     static constexpr bool CPLX = Traits<T>::cplx;
     using M = Mfma<R>;
     using v4 = typename M::v4;
     static constexpr uint32_t S = sizeof(T);
-    static constexpr int MAXS = MAXS_;   // superblocks per wave (the caller keeps RS <= GW MAXS)
+    static constexpr int MAXS = MAXS_;   // superblocks per pass
     // ring depth: as deep as 256 registers allow next to the accumulators
-    static constexpr int NS = MAXS <= 2 ? (CPLX ? 4 : (sizeof(R) == 8 ? 5 : 6)) : (!CPLX && sizeof(R) == 8 ? 3 : 4);
+    static constexpr int NS = MAXS == 1 ? (CPLX ? (sizeof(R) == 8 ? 4 : 5) : 8) : (CPLX ? 4 : (sizeof(R) == 8 ? 5 : 6));
     v4 acc[MAXS][2][2], aci[MAXS][2][2];
 
     __amdgpu_buffer_rsrc_t rs;
     uint32_t ld;
-    int n, kp, RS, gw, l16, g;
+    int n, kp, RS, sb0, l16, g;
+
+    __device__ __forceinline__ int sb_of(int s) const { return sb0 + GW * s; }
 
     __device__ __forceinline__ uint32_t off(int row, int col) const {
         return UPPER ? (uint32_t(row) * ld + uint32_t(col)) * S : (uint32_t(col) * ld + uint32_t(row)) * S;
@@ -324,7 +318,7 @@ struct PanelGemm {
     __device__ __forceinline__ void begin(int w) {
         static_for<0, MAXS>([&](auto ss) {
             constexpr int s = ss;
-            const int sb = gw + GW * s;
+            const int sb = sb_of(s);
             static_for<0, 2>([&](auto ee) {
                 static_for<0, 2>([&](auto cc) {
                     static_for<0, 4>([&](auto rr) {
@@ -345,7 +339,7 @@ struct PanelGemm {
     // turned into -S once the first operand loads are in flight
     template <bool FIRST>
     __device__ __forceinline__ void accumulate(int q0, int q1) {
-        if (q1 <= q0 || gw >= RS) {   // nothing to add, or no superblock on this wave
+        if (q1 <= q0 || sb0 >= RS) {   // nothing to add, or no superblock on this wave
             if constexpr (FIRST) negate_all();
             return;
         }
@@ -381,7 +375,7 @@ struct PanelGemm {
             load_pair(kp + 2 * l16, q + g, live, opa[st][0], opa[st][1]);
             static_for<0, MAXS>([&](auto ss) {
                 constexpr int s = ss;
-                const int row = kp + 32 * (gw + GW * s) + 2 * l16;
+                const int row = kp + 32 * sb_of(s) + 2 * l16;
                 load_pair(row, q + g, live, opb[st][s][0], opb[st][s][1]);
             });
         };
@@ -389,7 +383,7 @@ struct PanelGemm {
             constexpr int st = decltype(setc)::value;
             static_for<0, MAXS>([&](auto ss) {
                 constexpr int s = ss;
-                if (gw + GW * s < RS) {
+                if (sb_of(s) < RS) {
                     static_for<0, 2>([&](auto ee) {
                         static_for<0, 2>([&](auto cc) {
                             constexpr int e = ee, cb = cc;
@@ -414,24 +408,88 @@ struct PanelGemm {
             });
         }
     }
-    // P = -(accumulators) into the panel buffer
-    __device__ __forceinline__ void finish(T* pb, int w) {
+    // the diagonal block (superblock 0) as P into p11
+    __device__ __forceinline__ void finish_lds(T* p11, int w) {
+        negate_all();
+        static_for<0, 2>([&](auto ee) {
+            static_for<0, 2>([&](auto cc) {
+                static_for<0, 4>([&](auto rr) {
+                    constexpr int e = ee, cb = cc, r = rr;
+                    const int c = 2 * M::row(r, g) + cb;
+                    const int i = 2 * l16 + e;
+                    T val;
+                    if constexpr (CPLX) val = T{acc[0][e][cb][r], UPPER ? -aci[0][e][cb][r] : aci[0][e][cb][r]};
+                    else val = acc[0][e][cb][r];
+                    p11[i * LDD + c] = c < w ? val : zero<T>();
+                });
+            });
+        });
+    }
+    // Superblocks below the diagonal block, solved from the accumulators:
+    // L21 = P21 W^H, computed as L21^T = conj(W) P21^T on MFMA with the A
+    // operand from wm (wm[c' LDD + c] = conj(W(c', c))) and the B operand
+    // straight from the accumulators.  Register r of tile (e, cb) of lane
+    // (l16, g) holds P(i, c) at c = 2 row(r, g) + cb, four distinct c over the
+    // four lane groups, so step (r, cb) of the contraction runs over those c;
+    // W being lower triangular, the steps with every c >= 16 are skipped for
+    // c' < 16.  For complex Upper the accumulators hold conj(P) and W takes the
+    // place of conj(W), which gives conj(L21), the stored form.  The result
+    // tile (e, cp) holds L21(i, c') at c' = 16 cp + row(r, g), i = 32 sb + 2 l16 + e.
+    __device__ __forceinline__ void solve_store(const T* wm, int w) {
         negate_all();
         static_for<0, MAXS>([&](auto ss) {
             constexpr int s = ss;
-            const int sb = gw + GW * s;
+            const int sb = sb_of(s);
             if (sb < RS) {
-                static_for<0, 2>([&](auto ee) {
-                    static_for<0, 2>([&](auto cc) {
-                        static_for<0, 4>([&](auto rr) {
-                            constexpr int e = ee, cb = cc, r = rr;
-                            const int c = 2 * M::row(r, g) + cb;
-                            const int i = 32 * sb + 2 * l16 + e;
-                            T val;
-                            if constexpr (CPLX) val = T{acc[s][e][cb][r], UPPER ? -aci[s][e][cb][r] : aci[s][e][cb][r]};
-                            else val = acc[s][e][cb][r];
-                            pb[i * LDD + c] = c < w ? val : zero<T>();
+                static_for<0, 2>([&](auto pp) {
+                    constexpr int cp = pp;
+                    v4 x[2], xi[2];
+                    static_for<0, 2>([&](auto ee) {
+                        x[ee] = v4{R(0), R(0), R(0), R(0)};
+                        xi[ee] = v4{R(0), R(0), R(0), R(0)};
+                    });
+                    static_for<0, 4>([&](auto rr) {
+                        static_for<0, 2>([&](auto cc) {
+                            constexpr int r = rr, cb = cc;
+                            if constexpr (!(cp == 0 && 2 * M::row(r, 0) + cb >= 16)) {
+                                const int c = 2 * M::row(r, g) + cb;
+                                const T a = wm[(16 * cp + l16) * LDD + c];
+                                static_for<0, 2>([&](auto ee) {
+                                    constexpr int e = ee;
+                                    if constexpr (CPLX)
+                                        cmac<UPPER>(a.re, a.im, acc[s][e][cb][r], aci[s][e][cb][r], x[e], xi[e]);
+                                    else
+                                        x[e] = M::mac(a, acc[s][e][cb][r], x[e]);
+                                });
+                            }
                         });
+                    });
+                    static_for<0, 4>([&](auto rr) {
+                        constexpr int r = rr;
+                        const int col = 16 * cp + M::row(r, g);
+                        const int row = kp + 32 * sb + 2 * l16;
+                        if constexpr (PAIRED) {
+                            // rows row, row + 1 of one column with one 16-byte store (n even);
+                            // the elements are copied out before the bit cast (a bit cast
+                            // taken of the vector element itself was compiled into a
+                            // store of element 0 for every r)
+                            using V = uint32_t __attribute__((ext_vector_type(4)));
+                            using V2 = uint32_t __attribute__((ext_vector_type(2)));
+                            const R d0 = x[0][r], d1 = x[1][r];
+                            const V2 lo = __builtin_bit_cast(V2, d0), hi = __builtin_bit_cast(V2, d1);
+                            const bool st = row < n && col < w;
+                            __builtin_amdgcn_raw_buffer_store_b128(V{lo.x, lo.y, hi.x, hi.y}, rs,
+                                                                   st ? off(row, kp + col) : kBufOOB, 0, 0);
+                        } else {
+                            static_for<0, 2>([&](auto ee) {
+                                constexpr int e = ee;
+                                T val;
+                                if constexpr (CPLX) val = T{x[e][r], xi[e][r]};
+                                else val = x[e][r];
+                                const bool st = row + e < n && col < w;
+                                buf_store<T>(rs, st ? off(row + e, kp + col) : kBufOOB, val);
+                            });
+                        }
                     });
                 });
             }
@@ -439,33 +497,34 @@ struct PanelGemm {
     }
 };
 
-// One matrix, panel by panel, with look-ahead: wave 0 factors the diagonal
-// block of panel k while the other GW = WAVES - 1 waves already run the GEMM
-// of panel k + 32 over the columns left of k (final since earlier panels);
-// after the solve of panel k they add its 32 columns and write the new panel:
+// One matrix, panel by panel.  Per panel k:
 //
-//   GEMM(0) -> pb
-//   for k:  [wave 0: factor + invert pb's diagonal block | waves 1..: begin
-//            GEMM(k+32), add columns 0..k]  sync
-//           solve the rows below (all waves), L21 to memory  sync
-//           [waves 1..: add columns k..k+32, GEMM(k+32) -> pb]  sync
+//   wave 0:     GEMM of the diagonal block -> p11 (LDS); factor it, L11 to
+//               the matrix, the inverse W of L11 to LDS
+//   waves 1..3: GEMM of the first superblocks below (sb = w + 3 s, s < CH),
+//               kept in the accumulators
+//   sync
+//   waves 1..3: solve those from the accumulators, L21 to the matrix
+//   all waves:  the remaining superblocks, round-robin, CH at a time: GEMM,
+//               solve from the accumulators, L21 to the matrix
+//   sync
+//
+// P never leaves the registers, so the traffic per panel is S and the
+// columns of L left of k read, and L21 written.  The one-wave factorisation
+// overlaps the first GEMMs of the other three waves, and the workgroup is
+// small (four waves, under 40 KB of LDS), so that two matrices share a
+// compute unit and fill each other's gaps.
 template <typename T, bool UPPER, bool PAIRED>
 __device__ __forceinline__ void factor_matrix(__amdgpu_buffer_rsrc_t rs, uint32_t ld, int n,
-                                              int wave, T* pb, T* wm,
+                                              int wave, T* p11, T* wm,
                                               typename FactorType<T>::type* colx,
                                               typename Traits<typename FactorType<T>::type>::R* rdiag,
                                               int32_t* s_inf)
 {
     using R = typename Traits<T>::R;
     constexpr bool CPLX = Traits<T>::cplx;
-    using M = Mfma<R>;
-    using v4 = typename M::v4;
-    constexpr int GW = WAVES - 1;
-    constexpr int MAXT = Shape<T>::MAXT;
-    constexpr uint32_t S = sizeof(T);
-    auto off = [&](int row, int col) -> uint32_t {
-        return UPPER ? (uint32_t(row) * ld + uint32_t(col)) * S : (uint32_t(col) * ld + uint32_t(row)) * S;
-    };
+    constexpr int GW = WAVES - 1;                          // waves beside the factoring one
+    constexpr int CH = (CPLX && sizeof(R) == 8) ? 1 : 2;   // superblocks per pass
     // The lane index is re-read at every phase and hidden from the optimiser,
     // so that addresses derived from it are recomputed where they are used
     // instead of being hoisted and kept live (in registers) across phases.
@@ -474,207 +533,112 @@ __device__ __forceinline__ void factor_matrix(__amdgpu_buffer_rsrc_t rs, uint32_
         asm volatile("" : "+v"(lane));
         return lane;
     };
-    // ---- rows below the diagonal block of panel k: L21 = P21 W^H on MFMA,
-    // with P21 (rows) and conj(W) (columns) read from LDS
-    auto solve = [&](int k, int w) __attribute__((always_inline)) {
+    auto setup = [&](auto& gm, int k, int RS, int sb0) __attribute__((always_inline)) {
         const int lane = lane_now();
-        const int l16 = lane & 15, g = lane >> 4;
-        const int RB = (n - k + 15) >> 4;         // 16-row blocks of the panel
-        static_for<0, MAXT>([&](auto tt) {
-            constexpr int t = tt;
-            const int ib = wave + WAVES * t;
-            if (ib >= 2 && ib < RB) {
-                static_for<0, 2>([&](auto pp) {
-                    constexpr int cbp = pp;
-                    v4 x = {R(0), R(0), R(0), R(0)};
-                    v4 xi = {R(0), R(0), R(0), R(0)};
-                    static_for<0, 4 * (cbp + 1)>([&](auto uu) {   // W is lower triangular
-                        constexpr int u = uu;
-                        const int c = 4 * u + g;                  // contraction index
-                        const T ao = pb[(ib * 16 + l16) * LDD + c];
-                        const T bo = wm[(cbp * 16 + l16) * LDD + c];
-                        if constexpr (CPLX) cmac<false>(ao.re, ao.im, bo.re, bo.im, x, xi);
-                        else x = M::mac(ao, bo, x);
-                    });
-                    static_for<0, 4>([&](auto rr) {
-                        constexpr int r = rr;
-                        const int row = k + ib * 16 + M::row(r, g);
-                        const int col = cbp * 16 + l16;
-                        const bool st = row < n && col < w;
-                        T val;
-                        if constexpr (CPLX) val = T{x[r], UPPER ? -xi[r] : xi[r]};
-                        else val = x[r];
-                        buf_store<T>(rs, st ? off(row, k + col) : kBufOOB, val);
-                    });
-                });
-            }
-        });
-    };
-
-    auto factor_block = [&](int k, int w) __attribute__((always_inline)) {
-        const int lane = lane_now();
-        if constexpr (CPLX) factor_invert_inplace<T, UPPER>(pb, wm, rdiag, lane, k, n, w, rs, ld, *s_inf);
-        else factor_diag<T, UPPER>(pb, wm, colx, rdiag, lane, k, n, w, rs, ld, *s_inf);
-    };
-    // cdouble: no look-ahead (its accumulators for 7 waves, the operand ring
-    // and the solve do not fit in the registers together); every wave takes
-    // part in each panel's GEMM, then wave 0 factors, then all solve.
-    if constexpr (CPLX && sizeof(R) == 8) {
-        using G = PanelGemm<T, UPPER, PAIRED, WAVES>;
-        G gm;
         gm.rs = rs;
         gm.ld = ld;
         gm.n = n;
-        gm.gw = wave;
-        for (int k = 0; k < n; k += NBP) {
-            const int w = min(NBP, n - k);
-            const int lane = lane_now();
-            gm.l16 = lane & 15;
-            gm.g = lane >> 4;
-            gm.kp = k;
-            gm.RS = (n - k + 31) >> 5;
+        gm.kp = k;
+        gm.RS = RS;
+        gm.sb0 = sb0;
+        gm.l16 = lane & 15;
+        gm.g = lane >> 4;
+    };
+    // the superblocks from 3 CH + 1 on, after the sync
+    auto rest = [&](int k, int w, int RS) __attribute__((always_inline)) {
+        using G4 = PanelGemm<T, UPPER, PAIRED, WAVES, CH>;
+        for (int sb = GW * CH + 1 + wave; sb < RS; sb += WAVES * CH) {
+            G4 gm;
+            setup(gm, k, RS, sb);
             gm.begin(w);
             gm.template accumulate<true>(0, k);
-            gm.finish(pb, w);
-            __syncthreads();
-            if (wave == 0) factor_block(k, w);
-            __syncthreads();
-            solve(k, w);
-            __syncthreads();
+            gm.solve_store(wm, w);
         }
-        return;
-    }
-    // The two roles run separate copies of the panel loop with the same
-    // barriers, so that the GEMM accumulators do not exist on wave 0's path
-    // across the factorisation (which needs most of the registers).  The
-    // GEMM waves hold at most two superblocks each: the GEMMs of panels 0 and
-    // 32 (16 and 15 superblocks, and nothing to overlap with) run on all eight
-    // waves; from panel 64 on at most 14 superblocks remain for seven waves.
-    auto gemm_all = [&](int kp) __attribute__((always_inline)) {
-        using G8 = PanelGemm<T, UPPER, PAIRED, WAVES, 2>;
-        G8 g8;
-        const int lane = lane_now();
-        g8.rs = rs;
-        g8.ld = ld;
-        g8.n = n;
-        g8.gw = wave;
-        g8.l16 = lane & 15;
-        g8.g = lane >> 4;
-        g8.kp = kp;
-        g8.RS = (n - kp + 31) >> 5;
-        g8.begin(min(NBP, n - kp));
-        g8.template accumulate<true>(0, kp);
-        g8.finish(pb, min(NBP, n - kp));
     };
     if (wave == 0) {
-        gemm_all(0);
-        __syncthreads();
+        using G1 = PanelGemm<T, UPPER, PAIRED, 1, 1>;
         for (int k = 0; k < n; k += NBP) {
             const int w = min(NBP, n - k);
-            factor_block(k, w);
-            __syncthreads();
-            solve(k, w);
-            __syncthreads();   // the panel is in memory before the next GEMM reads it
-            if (k + NBP < n) {
-                if (k == 0) gemm_all(NBP);
-                __syncthreads();     // next panel's GEMM
+            const int RS = (n - k + 31) >> 5;
+            {
+                G1 gd;
+                setup(gd, k, 1, 0);
+                gd.begin(w);
+                gd.template accumulate<true>(0, k);
+                gd.finish_lds(p11, w);
             }
+            wave_lds_sync();
+            {
+                const int lane = lane_now();
+                if constexpr (CPLX) factor_invert_inplace<T, UPPER>(p11, wm, rdiag, lane, k, n, w, rs, ld, *s_inf);
+                else factor_diag<T, UPPER>(p11, wm, colx, rdiag, lane, k, n, w, rs, ld, *s_inf);
+            }
+            __syncthreads();
+            rest(k, w, RS);
+            __syncthreads();
         }
     } else {
-        using G = PanelGemm<T, UPPER, PAIRED, GW, 2>;
-        G gm;
-        gm.rs = rs;
-        gm.ld = ld;
-        gm.n = n;
-        gm.gw = wave - 1;
-        auto set_panel = [&](int kp) __attribute__((always_inline)) {
-            const int lane = lane_now();
-            gm.l16 = lane & 15;
-            gm.g = lane >> 4;
-            gm.kp = kp;
-            gm.RS = (n - kp + 31) >> 5;
-        };
-        gemm_all(0);
-        __syncthreads();
+        using G3 = PanelGemm<T, UPPER, PAIRED, GW, CH>;
         for (int k = 0; k < n; k += NBP) {
             const int w = min(NBP, n - k);
-            const int kn = k + NBP;
-            // the next panel's GEMM over the columns left of k (while wave 0
-            // factors the diagonal block of panel k)
-            if (kn < n && k > 0) {
-                set_panel(kn);
-                gm.begin(min(NBP, n - kn));
+            const int RS = (n - k + 31) >> 5;
+            G3 gm;
+            setup(gm, k, RS, wave);
+            const bool mine = wave < RS;
+            if (mine) {
+                gm.begin(w);
                 gm.template accumulate<true>(0, k);
             }
             __syncthreads();
-            solve(k, w);
+            if (mine) gm.solve_store(wm, w);
+            rest(k, w, RS);
             __syncthreads();
-            // add the columns of panel k, then P -> pb
-            if (kn < n) {
-                if (k == 0) {
-                    gemm_all(kn);
-                } else {
-                    set_panel(kn);
-                    gm.template accumulate<false>(k, kn);
-                    gm.finish(pb, min(NBP, n - kn));
-                }
-                __syncthreads();
-            }
         }
     }
 }
 
-// LDS: the panel buffer, then wm (the inverse of the diagonal block's factor), then the
+// LDS: the diagonal block P11 (then L11), conj of the inverse of L11, the
 // pivot exchange, 1 / L(j, j) and the info word
 template <typename T>
-constexpr int64_t aux_offset() { return int64_t(Shape<T>::MAXN) * LDD * sizeof(T); }
-template <typename T>
-constexpr int64_t aux_bytes() { return int64_t(NBP) * LDD * sizeof(T); }
-
-template <typename T, bool UPPER>
-__global__ __launch_bounds__(64 * WAVES) void potrf_blocked_kernel(
-    T* __restrict__ A, int n, int64_t lda, int64_t stride, int64_t batch,
-    int32_t* __restrict__ info)
-{
-    using R = typename Traits<T>::R;
+struct Smem {
     using C = typename FactorType<T>::type;
     using Rc = typename Traits<C>::R;
+    T p11[NBP * LDD];
+    T wm[NBP * LDD];
+    C colx[2 * NBP];
+    Rc rdiag[NBP];
+    int32_t inf;
+};
+
+template <typename T, bool UPPER>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
+void potrf_blocked_kernel(T* __restrict__ A, int n, int64_t lda, int64_t stride, int64_t batch,
+                          int32_t* __restrict__ info)
+{
+    using R = typename Traits<T>::R;
     constexpr bool CPLX = Traits<T>::cplx;
-    constexpr int MAXN = Shape<T>::MAXN;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    T* pb = reinterpret_cast<T*>(smem);       // the panel P, MAXN rows x LDD
-    T* wm = pb + MAXN * LDD;                  // conj of the inverse of the diagonal block's factor
-    C* colx = reinterpret_cast<C*>(smem + aux_offset<T>() + aux_bytes<T>());   // pivot exchange, 2 NBP
-    Rc* rdiag = reinterpret_cast<Rc*>(colx + 2 * NBP);   // 1 / L(j, j), NBP
-    int32_t* s_inf = reinterpret_cast<int32_t*>(rdiag + NBP);
+    __shared__ __attribute__((aligned(16))) Smem<T> sm;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t ld = uint32_t(lda);
     for (int64_t b = blockIdx.x; b < batch; b += gridDim.x) {
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(A + b * stride);
-        if (threadIdx.x == 0) *s_inf = 0;
+        if (threadIdx.x == 0) sm.inf = 0;
         // (the paired 16-byte loads are used for fp64 Lower with n even; the
         // fp32 pairs gave wrong results on the GPU and are not used)
         if constexpr (!UPPER && !CPLX && sizeof(R) == 8) {
-            if ((n & 1) == 0) factor_matrix<T, UPPER, true>(rs, ld, n, wave, pb, wm, colx, rdiag, s_inf);
-            else factor_matrix<T, UPPER, false>(rs, ld, n, wave, pb, wm, colx, rdiag, s_inf);
+            if ((n & 1) == 0) factor_matrix<T, UPPER, true>(rs, ld, n, wave, sm.p11, sm.wm, sm.colx, sm.rdiag, &sm.inf);
+            else factor_matrix<T, UPPER, false>(rs, ld, n, wave, sm.p11, sm.wm, sm.colx, sm.rdiag, &sm.inf);
         } else {
-            factor_matrix<T, UPPER, false>(rs, ld, n, wave, pb, wm, colx, rdiag, s_inf);
+            factor_matrix<T, UPPER, false>(rs, ld, n, wave, sm.p11, sm.wm, sm.colx, sm.rdiag, &sm.inf);
         }
-        if (threadIdx.x == 0 && info != nullptr) info[b] = *s_inf;
+        if (threadIdx.x == 0 && info != nullptr) info[b] = sm.inf;
         __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------- host side
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
-
-template <typename T>
-constexpr int64_t lds_bytes() {
-    using C = typename FactorType<T>::type;
-    using Rc = typename Traits<C>::R;
-    return aux_offset<T>() + aux_bytes<T>() + 2 * NBP * sizeof(C) + NBP * sizeof(Rc) + 16;
-}
 
 template <typename T>
 bool supported_t(int n, int64_t lda) {
@@ -689,43 +653,17 @@ bool geometry_t(int n, int64_t batch, Geometry& g) {
     g.threads = 64 * WAVES;
     g.panel = NBP;
     g.grid = batch < kMaxGrid ? batch : kMaxGrid;
-    g.lds = lds_bytes<T>();
+    g.lds = int64_t(sizeof(Smem<T>));
     return true;
-}
-
-// The dynamic LDS limit is raised once per kernel and device (the attribute
-// stays set; doing it at every call would also put a non-stream call inside
-// a caller's stream capture).  Concurrent first calls may both set it, which
-// is harmless.
-template <typename K>
-hipError_t allow_lds(K kernel, size_t shm) {
-    static std::atomic<uint32_t> done{0};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    const uint32_t bit = dev < 32 ? (1u << dev) : 0u;
-    if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(shm));
-    if (e == hipSuccess) done.fetch_or(bit, std::memory_order_relaxed);
-    return e;
 }
 
 template <typename T>
 hipError_t potrf_t(bool upper, int n, void* A, int64_t lda, int64_t stride, int64_t batch,
                    int32_t* info, hipStream_t s) {
-    static_assert(lds_bytes<T>() <= 160 * 1024, "LDS per workgroup");
     const dim3 gd((unsigned)(batch < kMaxGrid ? batch : kMaxGrid)), bd(64 * WAVES);
     T* a = static_cast<T*>(A);
-    const size_t shm = size_t(lds_bytes<T>());
-    if (upper) {
-        hipError_t e = allow_lds(potrf_blocked_kernel<T, true>, shm);
-        if (e != hipSuccess) return e;
-        return launch(potrf_blocked_kernel<T, true>, gd, bd, shm, s, a, n, lda, stride, batch, info);
-    }
-    hipError_t e = allow_lds(potrf_blocked_kernel<T, false>, shm);
-    if (e != hipSuccess) return e;
-    return launch(potrf_blocked_kernel<T, false>, gd, bd, shm, s, a, n, lda, stride, batch, info);
+    if (upper) return launch(potrf_blocked_kernel<T, true>, gd, bd, 0, s, a, n, lda, stride, batch, info);
+    return launch(potrf_blocked_kernel<T, false>, gd, bd, 0, s, a, n, lda, stride, batch, info);
 }
 
 }  // namespace blocked_detail

@@ -129,12 +129,12 @@ def test_posv_auto_routes_beyond_the_window_to_split(lib):
     assert bl.route("f64", "U", 200, 64, nrhs=1)["family"] == "posv_split"
     assert bl.route("c64", "U", 512, 64, nrhs=3)["family"] == "posv_split"
     with pytest.raises(bl.BatchlasError) as e:
-        bl.route("c128", "L", 300, 4, nrhs=1)      # no potrf family for this shape
+        bl.route("c128", "L", 600, 4, nrhs=1)      # no potrf family for this shape
     assert e.value.status_name == "NOT_SUPPORTED"
 
 
 def test_route_beyond_every_family_is_not_supported(lib):
-    for dt, n in (("c128", 257), ("c64", 513), ("f64", 513), ("f32", 1000)):
+    for dt, n in (("c128", 513), ("c64", 513), ("f64", 513), ("f32", 1000)):
         with pytest.raises(bl.BatchlasError) as e:
             bl.route(dt, "L", n, 4)
         assert e.value.status_name == "NOT_SUPPORTED"
