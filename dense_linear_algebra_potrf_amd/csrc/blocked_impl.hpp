@@ -282,7 +282,7 @@ __device__ __forceinline__ void factor_invert_inplace(T* pb, T* wm, typename Tra
 // runs on the stored values, conj(S) and conj(L), which gives conj(P): the
 // stored form of P, as it is written back to the matrix; the block for LDS is
 // conjugated.
-template <typename T, bool UPPER, bool PAIRED, int GW, int MAXS_>
+template <typename T, bool UPPER, bool PAIRED, int GW, int MAXS_, int NCB_ = 2>
 struct PanelGemm {
     using R = typename Traits<T>::R;
     static constexpr bool CPLX = Traits<T>::cplx;
@@ -290,9 +290,15 @@ struct PanelGemm {
     using v4 = typename M::v4;
     static constexpr uint32_t S = sizeof(T);
     static constexpr int MAXS = MAXS_;   // superblocks per pass
+    static constexpr int NCB = NCB_;     // column tiles: 2 for 32 columns, 4 for 64
     // ring depth: as deep as 256 registers allow next to the accumulators
-    static constexpr int NS = MAXS == 1 ? (CPLX ? (sizeof(R) == 8 ? 4 : 5) : 8) : (CPLX ? 4 : (sizeof(R) == 8 ? 5 : 6));
-    v4 acc[MAXS][2][2], aci[MAXS][2][2];
+    static constexpr int NS = (NCB + 2 * MAXS) <= 4 ? (CPLX ? (sizeof(R) == 8 ? 4 : 5) : 8)
+                                                    : (CPLX ? 4 : (sizeof(R) == 8 ? 5 : 6));
+    v4 acc[MAXS][2][NCB], aci[MAXS][2][NCB];
+    // column of register r of column tile cb (lane group g)
+    static __device__ __forceinline__ int col_of(int r, int g, int cb) {
+        return 32 * (cb >> 1) + 2 * M::row(r, g) + (cb & 1);
+    }
 
     __amdgpu_buffer_rsrc_t rs;
     uint32_t ld;
@@ -306,7 +312,7 @@ struct PanelGemm {
     __device__ __forceinline__ void negate_all() {
         static_for<0, MAXS>([&](auto ss) {
             static_for<0, 2>([&](auto ee) {
-                static_for<0, 2>([&](auto cc) {
+                static_for<0, NCB>([&](auto cc) {
                     acc[ss][ee][cc] = -acc[ss][ee][cc];
                     if constexpr (CPLX) aci[ss][ee][cc] = -aci[ss][ee][cc];
                 });
@@ -320,10 +326,10 @@ struct PanelGemm {
             constexpr int s = ss;
             const int sb = sb_of(s);
             static_for<0, 2>([&](auto ee) {
-                static_for<0, 2>([&](auto cc) {
+                static_for<0, NCB>([&](auto cc) {
                     static_for<0, 4>([&](auto rr) {
                         constexpr int e = ee, cb = cc, r = rr;
-                        const int c = 2 * M::row(r, g) + cb;
+                        const int c = col_of(r, g, cb);
                         const int i = 32 * sb + 2 * l16 + e;
                         const bool ref = sb < RS && kp + i < n && c < w && i >= c;
                         const T x = buf_load<T>(rs, ref ? off(kp + i, kp + c) : kBufOOB);
@@ -343,7 +349,7 @@ struct PanelGemm {
             if constexpr (FIRST) negate_all();
             return;
         }
-        T opa[NS][2], opb[NS][MAXS][2];
+        T opa[NS][NCB], opb[NS][MAXS][2];
         // A masked lane gets bit 31 set in its offset, which puts it out of the
         // buffer's range (no memory access, the load returns 0).  The mask is
         // applied arithmetically, from a value the optimiser cannot see
@@ -372,7 +378,10 @@ struct PanelGemm {
         auto load_ops = [&](int q, auto setc) __attribute__((always_inline)) {
             constexpr int st = decltype(setc)::value;
             const bool live = q < q1;
-            load_pair(kp + 2 * l16, q + g, live, opa[st][0], opa[st][1]);
+            static_for<0, NCB / 2>([&](auto hh) {
+                constexpr int h = hh;
+                load_pair(kp + 32 * h + 2 * l16, q + g, live, opa[st][2 * h], opa[st][2 * h + 1]);
+            });
             static_for<0, MAXS>([&](auto ss) {
                 constexpr int s = ss;
                 const int row = kp + 32 * sb_of(s) + 2 * l16;
@@ -385,7 +394,7 @@ struct PanelGemm {
                 constexpr int s = ss;
                 if (sb_of(s) < RS) {
                     static_for<0, 2>([&](auto ee) {
-                        static_for<0, 2>([&](auto cc) {
+                        static_for<0, NCB>([&](auto cc) {
                             constexpr int e = ee, cb = cc;
                             const T& a = opa[st][cb];
                             const T& bv = opb[st][s][e];
@@ -410,6 +419,7 @@ struct PanelGemm {
     }
     // the diagonal block (superblock 0) as P into p11
     __device__ __forceinline__ void finish_lds(T* p11, int w) {
+        static_assert(NCB == 2, "32 columns");
         negate_all();
         static_for<0, 2>([&](auto ee) {
             static_for<0, 2>([&](auto cc) {
@@ -436,6 +446,7 @@ struct PanelGemm {
     // place of conj(W), which gives conj(L21), the stored form.  The result
     // tile (e, cp) holds L21(i, c') at c' = 16 cp + row(r, g), i = 32 sb + 2 l16 + e.
     __device__ __forceinline__ void solve_store(const T* wm, int w) {
+        static_assert(NCB == 2, "32 columns");
         negate_all();
         static_for<0, MAXS>([&](auto ss) {
             constexpr int s = ss;
@@ -494,6 +505,82 @@ struct PanelGemm {
                 });
             }
         });
+    }
+
+    // ---- 64-column passes (real types): NCB = 4, one superblock
+    // A superblock below the 64 x 64 diagonal block, solved from the
+    // accumulators in two stages: L_a = P_a W1^T for the first 32 columns (as
+    // solve_store), then P_b -= L_a L21'^T on MFMA with L21' (rows 32..63,
+    // columns 0..31 of the diagonal block's factor) from LDS as the A operand
+    // and L_a straight from the first stage's result registers as the B
+    // operand: register r' of result tile (e, cp) holds L_a(i, c') at
+    // c' = 16 cp + row(r', g), four distinct c' over the lane groups, so step
+    // (cp, r') of that contraction runs over them.  Then L_b = P_b W2^T.
+    __device__ __forceinline__ void solve_store2(const T* wm1, const T* wm2, const T* pl, int w) {
+        static_assert(NCB == 4 && MAXS == 1 && !CPLX, "64 columns, real");
+        negate_all();
+        const int sb = sb0;
+        if (sb >= RS) return;
+        const int row = kp + 32 * sb + 2 * l16;
+        auto store_pair = [&](int col, bool colok, R v0, R v1) __attribute__((always_inline)) {
+            if constexpr (PAIRED) {
+                using V = uint32_t __attribute__((ext_vector_type(4)));
+                using V2 = uint32_t __attribute__((ext_vector_type(2)));
+                const V2 lo = __builtin_bit_cast(V2, v0), hi = __builtin_bit_cast(V2, v1);
+                const bool st = row < n && colok;
+                __builtin_amdgcn_raw_buffer_store_b128(V{lo.x, lo.y, hi.x, hi.y}, rs,
+                                                       st ? off(row, kp + col) : kBufOOB, 0, 0);
+            } else {
+                buf_store<T>(rs, row < n && colok ? off(row, kp + col) : kBufOOB, T(v0));
+                buf_store<T>(rs, row + 1 < n && colok ? off(row + 1, kp + col) : kBufOOB, T(v1));
+            }
+        };
+        // one 32-column half: x[cp][e] = P(half) W^T from the accumulator tiles 2 h, 2 h + 1
+        auto half = [&](auto hh, const T* wmh, v4 (&x)[2][2]) __attribute__((always_inline)) {
+            constexpr int h = hh;
+            static_for<0, 2>([&](auto pp) {
+                constexpr int cp = pp;
+                static_for<0, 2>([&](auto ee) { x[cp][ee] = v4{R(0), R(0), R(0), R(0)}; });
+                static_for<0, 4>([&](auto rr) {
+                    static_for<0, 2>([&](auto cc) {
+                        constexpr int r = rr, cb = cc;
+                        if constexpr (!(cp == 0 && 2 * M::row(r, 0) + cb >= 16)) {
+                            const int c = 2 * M::row(r, g) + cb;
+                            const T a = wmh[(16 * cp + l16) * LDD + c];
+                            static_for<0, 2>([&](auto ee) {
+                                constexpr int e = ee;
+                                x[cp][e] = M::mac(a, acc[0][e][2 * h + cb][r], x[cp][e]);
+                            });
+                        }
+                    });
+                });
+                static_for<0, 4>([&](auto rr) {
+                    constexpr int r = rr;
+                    const int col = 16 * cp + M::row(r, g);
+                    const R d0 = x[cp][0][r], d1 = x[cp][1][r];
+                    store_pair(32 * h + col, 32 * h + col < w, d0, d1);
+                });
+            });
+        };
+        v4 xa[2][2];
+        half(ic<0>{}, wm1, xa);
+        // P_b -= L_a L21'^T
+        static_for<0, 2>([&](auto pp) {
+            static_for<0, 4>([&](auto rr) {
+                constexpr int cp = pp, r = rr;
+                const int cpr = 16 * cp + M::row(r, g);
+                static_for<0, 2>([&](auto cc) {
+                    constexpr int cb = cc;
+                    const T a = -pl[(2 * l16 + cb) * LDD + cpr];
+                    static_for<0, 2>([&](auto ee) {
+                        constexpr int e = ee;
+                        acc[0][e][2 + cb] = M::mac(a, xa[cp][e][r], acc[0][e][2 + cb]);
+                    });
+                });
+            });
+        });
+        v4 xb[2][2];
+        half(ic<1>{}, wm2, xb);
     }
 };
 
@@ -597,14 +684,190 @@ __device__ __forceinline__ void factor_matrix(__amdgpu_buffer_rsrc_t rs, uint32_
     }
 }
 
+// Real types: 64-column panels.  The left-looking GEMM streams the columns
+// of L left of k once per panel, so twice the panel width halves that
+// traffic.  The 64 x 64 diagonal block is three 32 x 32 GEMM units (D11 =
+// rows 0..31 x columns 0..31, D21 = rows 32..63 x columns 0..31, D22 = rows
+// 32..63 x columns 32..63, all over the columns of L left of k) and two
+// 32 x 32 factorisations.  Per panel k (64 columns):
+//
+//   wave 0:     D11 -> p11; factor it (L11, W1)     | wave 1: D21 -> pa
+//   wave 2:     D22 -> p22                          | wave 3: GEMM of superblock 2
+//   sync
+//   wave 0:     L21' = P21' W1^T on MFMA (to the matrix and to pl);
+//               P22 -= L21' L21'^T on MFMA; factor P22 (L22, W2)
+//   waves 1, 2: GEMM of superblocks 3, 4 (wave 3 keeps superblock 2)
+//   sync
+//   waves 1..3: solve the kept superblock from the accumulators in two
+//               stages (solve_store2)
+//   all waves:  the remaining superblocks, round-robin: GEMM, two-stage solve
+//   sync
+template <typename T, bool UPPER, bool PAIRED>
+__device__ __forceinline__ void factor_matrix_wide(__amdgpu_buffer_rsrc_t rs, uint32_t ld, int n,
+                                                   int wave, T* p11, T* wm1, T* pa, T* p22, T* pl,
+                                                   T* wm2, double* colx, double* rdiag,
+                                                   int32_t* s_inf)
+{
+    using R = typename Traits<T>::R;
+    using M = Mfma<R>;
+    using v4 = typename M::v4;
+    static_assert(!Traits<T>::cplx, "real types");
+    constexpr uint32_t S = sizeof(T);
+    auto off = [&](int row, int col) -> uint32_t {
+        return UPPER ? (uint32_t(row) * ld + uint32_t(col)) * S : (uint32_t(col) * ld + uint32_t(row)) * S;
+    };
+    auto lane_now = [&]() __attribute__((always_inline)) {
+        int lane = threadIdx.x & 63;
+        asm volatile("" : "+v"(lane));
+        return lane;
+    };
+    auto setup = [&](auto& gm, int k, int RS, int sb0) __attribute__((always_inline)) {
+        const int lane = lane_now();
+        gm.rs = rs;
+        gm.ld = ld;
+        gm.n = n;
+        gm.kp = k;
+        gm.RS = RS;
+        gm.sb0 = sb0;
+        gm.l16 = lane & 15;
+        gm.g = lane >> 4;
+    };
+    using G1 = PanelGemm<T, UPPER, PAIRED, 1, 1>;
+    using G64 = PanelGemm<T, UPPER, PAIRED, 1, 1, 4>;
+    // a 32 x 32 unit of the diagonal block: rows 32 sb.. of the panel at kp,
+    // its columns 0..31, over the columns of L left of q1, into dst
+    auto unit = [&](int kp, int RS, int sb, int w, int q1, T* dst) __attribute__((always_inline)) {
+        G1 gd;
+        setup(gd, kp, RS, sb);
+        gd.begin(w);
+        gd.template accumulate<true>(0, q1);
+        gd.finish_lds(dst, w);
+    };
+    // the superblocks from 5 on, round-robin over the four waves
+    auto rest = [&](int k, int w, int RS) __attribute__((always_inline)) {
+        for (int sb = 5 + wave; sb < RS; sb += WAVES) {
+            G64 gm;
+            setup(gm, k, RS, sb);
+            gm.begin(w);
+            gm.template accumulate<true>(0, k);
+            gm.solve_store2(wm1, wm2, pl, w);
+        }
+    };
+    // (each role runs its own copy of the panel loop with the same syncs: in
+    // one loop the compiler keeps the roles' values live together)
+    if (wave == 0) {
+        for (int k = 0; k < n; k += 2 * NBP) {
+            const int w = min(2 * NBP, n - k);
+            const int wa = min(NBP, w), wb = w - NBP;    // wb <= 0: no second half
+            const int RS = (n - k + 31) >> 5;
+            unit(k, 1, 0, wa, k, p11);
+            wave_lds_sync();
+            factor_diag<T, UPPER>(p11, wm1, colx, rdiag, lane_now(), k, n, wa, rs, ld, *s_inf);
+            __syncthreads();
+            if (wb > 0) {
+                const int lane = lane_now();
+                const int l16 = lane & 15, g = lane >> 4;
+                // L21' = P21' W1^T (both operands from LDS), to the matrix and to pl
+                static_for<0, 2>([&](auto bb) {
+                    constexpr int ib = bb;
+                    static_for<0, 2>([&](auto pp) {
+                        constexpr int cbp = pp;
+                        v4 x = {R(0), R(0), R(0), R(0)};
+                        static_for<0, 4 * (cbp + 1)>([&](auto uu) {   // W1 is lower triangular
+                            constexpr int u = uu;
+                            const int c = 4 * u + g;
+                            x = M::mac(pa[(ib * 16 + l16) * LDD + c], wm1[(cbp * 16 + l16) * LDD + c], x);
+                        });
+                        static_for<0, 4>([&](auto rr) {
+                            constexpr int r = rr;
+                            const int i = ib * 16 + M::row(r, g);
+                            const int c = cbp * 16 + l16;
+                            const T v = x[r];
+                            pl[i * LDD + c] = v;
+                            const bool st = k + NBP + i < n && c < wa;
+                            buf_store<T>(rs, st ? off(k + NBP + i, k + c) : kBufOOB, v);
+                        });
+                    });
+                });
+                wave_lds_sync();
+                // P22 -= L21' L21'^T (lower tiles)
+                static_for<0, 3>([&](auto tt) {
+                    constexpr int mt = tt == 0 ? 0 : 1, nt = tt == 2 ? 1 : 0;
+                    v4 x = {R(0), R(0), R(0), R(0)};
+                    static_for<0, NBP / 4>([&](auto uu) {
+                        constexpr int u = uu;
+                        const int c = 4 * u + g;
+                        x = M::mac(pl[(16 * mt + l16) * LDD + c], pl[(16 * nt + l16) * LDD + c], x);
+                    });
+                    static_for<0, 4>([&](auto rr) {
+                        constexpr int r = rr;
+                        T& d = p22[(16 * mt + M::row(r, g)) * LDD + 16 * nt + l16];
+                        d = d - T(x[r]);
+                    });
+                });
+                wave_lds_sync();
+                factor_diag<T, UPPER>(p22, wm2, colx, rdiag, lane_now(), k + NBP, n, wb, rs, ld, *s_inf);
+            }
+            __syncthreads();
+            rest(k, w, RS);
+            __syncthreads();
+        }
+    } else if (wave < 3) {
+        for (int k = 0; k < n; k += 2 * NBP) {
+            const int w = min(2 * NBP, n - k);
+            const int wa = min(NBP, w), wb = w - NBP;
+            const int RS = (n - k + 31) >> 5;
+            if (wb > 0) {
+                if (wave == 1) unit(k, 2, 1, wa, k, pa);            // D21
+                else unit(k + NBP, 1, 0, wb, k, p22);               // D22
+            }
+            __syncthreads();
+            {
+                G64 gm;
+                setup(gm, k, RS, wave + 2);
+                const bool mine = wave + 2 < RS;
+                if (mine) {
+                    gm.begin(w);
+                    gm.template accumulate<true>(0, k);
+                }
+                __syncthreads();
+                if (mine) gm.solve_store2(wm1, wm2, pl, w);
+            }
+            rest(k, w, RS);
+            __syncthreads();
+        }
+    } else {
+        for (int k = 0; k < n; k += 2 * NBP) {
+            const int w = min(2 * NBP, n - k);
+            const int RS = (n - k + 31) >> 5;
+            {
+                G64 gm;
+                setup(gm, k, RS, 2);
+                const bool mine = 2 < RS;
+                if (mine) {
+                    gm.begin(w);
+                    gm.template accumulate<true>(0, k);
+                }
+                __syncthreads();
+                __syncthreads();
+                if (mine) gm.solve_store2(wm1, wm2, pl, w);
+            }
+            rest(k, w, RS);
+            __syncthreads();
+        }
+    }
+}
+
 // LDS: the diagonal block P11 (then L11), conj of the inverse of L11, the
 // pivot exchange, 1 / L(j, j) and the info word
 template <typename T>
 struct Smem {
     using C = typename FactorType<T>::type;
     using Rc = typename Traits<C>::R;
+    static constexpr int WIDE = Traits<T>::cplx ? 1 : NBP * LDD;   // 64-column panels (real types)
     T p11[NBP * LDD];
     T wm[NBP * LDD];
+    T pa[WIDE], p22[WIDE], pl[WIDE], wm2[WIDE];
     C colx[2 * NBP];
     Rc rdiag[NBP];
     int32_t inf;
@@ -626,11 +889,18 @@ void potrf_blocked_kernel(T* __restrict__ A, int n, int64_t lda, int64_t stride,
         if (threadIdx.x == 0) sm.inf = 0;
         // (the paired 16-byte loads are used for fp64 Lower with n even; the
         // fp32 pairs gave wrong results on the GPU and are not used)
-        if constexpr (!UPPER && !CPLX && sizeof(R) == 8) {
-            if ((n & 1) == 0) factor_matrix<T, UPPER, true>(rs, ld, n, wave, sm.p11, sm.wm, sm.colx, sm.rdiag, &sm.inf);
-            else factor_matrix<T, UPPER, false>(rs, ld, n, wave, sm.p11, sm.wm, sm.colx, sm.rdiag, &sm.inf);
-        } else {
+        if constexpr (CPLX) {
             factor_matrix<T, UPPER, false>(rs, ld, n, wave, sm.p11, sm.wm, sm.colx, sm.rdiag, &sm.inf);
+        } else if constexpr (!UPPER && sizeof(R) == 8) {
+            if ((n & 1) == 0)
+                factor_matrix_wide<T, UPPER, true>(rs, ld, n, wave, sm.p11, sm.wm, sm.pa, sm.p22, sm.pl, sm.wm2,
+                                                   sm.colx, sm.rdiag, &sm.inf);
+            else
+                factor_matrix_wide<T, UPPER, false>(rs, ld, n, wave, sm.p11, sm.wm, sm.pa, sm.p22, sm.pl, sm.wm2,
+                                                    sm.colx, sm.rdiag, &sm.inf);
+        } else {
+            factor_matrix_wide<T, UPPER, false>(rs, ld, n, wave, sm.p11, sm.wm, sm.pa, sm.p22, sm.pl, sm.wm2,
+                                                sm.colx, sm.rdiag, &sm.inf);
         }
         if (threadIdx.x == 0 && info != nullptr) info[b] = sm.inf;
         __syncthreads();
