@@ -691,12 +691,12 @@ __device__ __forceinline__ void factor_matrix(__amdgpu_buffer_rsrc_t rs, uint32_
 // 32..63 x columns 32..63, all over the columns of L left of k) and two
 // 32 x 32 factorisations.  Per panel k (64 columns):
 //
-//   wave 0:     D11 -> p11; factor it (L11, W1)     | wave 1: D21 -> pa
-//   wave 2:     D22 -> p22                          | wave 3: GEMM of superblock 2
+//   waves 1..3: D11 -> p11, D21 -> pa, D22 -> p22
 //   sync
-//   wave 0:     L21' = P21' W1^T on MFMA (to the matrix and to pl);
-//               P22 -= L21' L21'^T on MFMA; factor P22 (L22, W2)
-//   waves 1, 2: GEMM of superblocks 3, 4 (wave 3 keeps superblock 2)
+//   wave 0:     factor P11 (L11, W1); L21' = P21' W1^T on MFMA (to the
+//               matrix and to pl); P22 -= L21' L21'^T on MFMA; factor P22
+//               (L22, W2)
+//   waves 1..3: GEMM of superblocks 2..4, kept in the accumulators
 //   sync
 //   waves 1..3: solve the kept superblock from the accumulators in two
 //               stages (solve_store2)
@@ -760,11 +760,10 @@ __device__ __forceinline__ void factor_matrix_wide(__amdgpu_buffer_rsrc_t rs, ui
             const int w = min(2 * NBP, n - k);
             const int wa = min(NBP, w), wb = w - NBP;    // wb <= 0: no second half
             const int RS = (n - k + 31) >> 5;
-            unit(k, 1, 0, wa, k, p11);
-            wave_lds_sync();
-            factor_diag<T, UPPER>(p11, wm1, colx, rdiag, lane_now(), k, n, wa, rs, ld, *s_inf);
             __syncthreads();
+            factor_diag<T, UPPER>(p11, wm1, colx, rdiag, lane_now(), k, n, wa, rs, ld, *s_inf);
             if (wb > 0) {
+                wave_lds_sync();
                 const int lane = lane_now();
                 const int l16 = lane & 15, g = lane >> 4;
                 // L21' = P21' W1^T (both operands from LDS), to the matrix and to pl
@@ -812,43 +811,25 @@ __device__ __forceinline__ void factor_matrix_wide(__amdgpu_buffer_rsrc_t rs, ui
             rest(k, w, RS);
             __syncthreads();
         }
-    } else if (wave < 3) {
+    } else {
         for (int k = 0; k < n; k += 2 * NBP) {
             const int w = min(2 * NBP, n - k);
             const int wa = min(NBP, w), wb = w - NBP;
             const int RS = (n - k + 31) >> 5;
-            if (wb > 0) {
-                if (wave == 1) unit(k, 2, 1, wa, k, pa);            // D21
-                else unit(k + NBP, 1, 0, wb, k, p22);               // D22
+            if (wave == 1) unit(k, 1, 0, wa, k, p11);                       // D11
+            else if (wb > 0) {
+                if (wave == 2) unit(k, 2, 1, wa, k, pa);                    // D21
+                else unit(k + NBP, 1, 0, wb, k, p22);                       // D22
             }
             __syncthreads();
             {
                 G64 gm;
-                setup(gm, k, RS, wave + 2);
-                const bool mine = wave + 2 < RS;
+                setup(gm, k, RS, wave + 1);
+                const bool mine = wave + 1 < RS;
                 if (mine) {
                     gm.begin(w);
                     gm.template accumulate<true>(0, k);
                 }
-                __syncthreads();
-                if (mine) gm.solve_store2(wm1, wm2, pl, w);
-            }
-            rest(k, w, RS);
-            __syncthreads();
-        }
-    } else {
-        for (int k = 0; k < n; k += 2 * NBP) {
-            const int w = min(2 * NBP, n - k);
-            const int RS = (n - k + 31) >> 5;
-            {
-                G64 gm;
-                setup(gm, k, RS, 2);
-                const bool mine = 2 < RS;
-                if (mine) {
-                    gm.begin(w);
-                    gm.template accumulate<true>(0, k);
-                }
-                __syncthreads();
                 __syncthreads();
                 if (mine) gm.solve_store2(wm1, wm2, pl, w);
             }
