@@ -137,23 +137,36 @@ __device__ __forceinline__ void factor_diag(T* pb, T* wm, double* colx, double* 
     colx[i] = v[0];
     wave_lds_sync();
     const uint32_t cxo = lds_offset(colx);
+    // a lane's value of x, read by the whole wave (two 32-bit lane reads)
+    auto lane_read = [](double x, int src) __attribute__((always_inline)) {
+        const uint64_t u = __builtin_bit_cast(uint64_t, x);
+        const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(u), src);
+        const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(u >> 32), src);
+        return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+    };
     static_for<0, NBP>([&](auto jj) {
         constexpr int j = jj;
-        // column j, published at step j - 1 (its reads stay in this step),
-        // read in one batch: consumed one by one, the reads would each wait
-        // for the previous one
-        const lds_cptr<double> col = lds_after<double>(cxo + uint32_t((j & 1) * NBP) * 8u, v[j]);
+        // The pivot S(j, j) and S(j + 1, j), which the next pivot's chain
+        // needs, are read from lanes j and j + 1 directly; the rest of column
+        // j (rows j + 2..), published at step j - 1, comes from LDS in one
+        // batch (consumed one by one, the reads would each wait for the
+        // previous one), off that chain.
+        const double d = lane_read(v[j], j);
+        double s1 = 0.0;
+        if constexpr (j + 1 < NBP) s1 = lane_read(v[j], j + 1);
         double cv[NBP];
-        static_for<j, NBP>([&](auto mm) { cv[mm] = col[mm]; });
+        if constexpr (j + 2 < NBP) {
+            const lds_cptr<double> col = lds_after<double>(cxo + uint32_t((j & 1) * NBP) * 8u, v[j]);
+            static_for<j + 2, NBP>([&](auto mm) { cv[mm] = col[mm]; });
+        }
         __builtin_amdgcn_sched_barrier(0);
-        const double d = cv[j];
         if (j < w) inf = (inf == 0 && !(d > 0.0)) ? (k + j + 1) : inf;
         double sq, rsd;
         pivot_sqrt_rsq(d, sq, rsd);
         const double beta = v[j] * (rsd * rsd);       // S(i, j) / d
         // rows at or above j only touch slots right of the diagonal (unused)
         if constexpr (j + 1 < NBP) {
-            v[j + 1] = __builtin_fma(-beta, cv[j + 1], v[j + 1]);
+            v[j + 1] = __builtin_fma(-beta, s1, v[j + 1]);
             colx[((j + 1) & 1) * NBP + i] = v[j + 1];
         }
         static_for<j + 2, NBP>([&](auto mm) {
