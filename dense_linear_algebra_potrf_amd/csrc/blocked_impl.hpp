@@ -192,20 +192,24 @@ __device__ __forceinline__ void factor_diag(T* pb, T* wm, double* colx, double* 
     //     W(m, i) = (delta(m, i) - sum_{p < m} L(m, p) W(p, i)) / L(m, m),
     // from the stored factor (as the solve will use it); columns are
     // independent, so no exchange between lanes is needed.  Row m of L11 is
-    // read in one batch, and the sum runs as four interleaved partial sums.
+    // read in one batch while row m - 1 is summed, and the sum runs as four
+    // interleaved partial sums.
     const uint32_t pbo = lds_offset(pb);
     double x[NBP];
+    double lr[2][NBP];   // row m in lr[m & 1], row m + 1 arriving in the other
     static_for<0, NBP>([&](auto mm) {
         constexpr int m = mm;
-        const lds_cptr<T> row = lds_after<T>(pbo + uint32_t(m * LDD) * uint32_t(sizeof(T)), x[m > 0 ? m - 1 : 0]);
-        double lr[NBP];
-        static_for<0, m>([&](auto pp) { lr[pp] = double(row[pp]); });
+        if constexpr (m + 1 < NBP) {
+            const lds_cptr<T> row = lds_after<T>(pbo + uint32_t((m + 1) * LDD) * uint32_t(sizeof(T)),
+                                                 x[m > 0 ? m - 1 : 0]);
+            static_for<0, m + 1>([&](auto pp) { lr[(m + 1) & 1][pp] = double(row[pp]); });
+        }
         const double rd = rdiag[m];
         __builtin_amdgcn_sched_barrier(0);
         double acc[4] = {(m == i) ? 1.0 : 0.0, 0.0, 0.0, 0.0};
         static_for<0, m>([&](auto pp) {
             constexpr int p = pp;
-            acc[p & 3] = __builtin_fma(-lr[p], x[p], acc[p & 3]);
+            acc[p & 3] = __builtin_fma(-lr[m & 1][p], x[p], acc[p & 3]);
         });
         x[m] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * rd;
     });
