@@ -309,7 +309,7 @@ struct PanelGemm {
     static constexpr int MAXS = MAXS_;   // superblocks per pass
     static constexpr int NCB = NCB_;     // column tiles: 2 for 32 columns, 4 for 64
     // ring depth: as deep as 256 registers allow next to the accumulators
-    static constexpr int NS = (NCB + 2 * MAXS) <= 4 ? (CPLX ? (sizeof(R) == 8 ? 4 : 5) : 8)
+    static constexpr int NS = NCB == 4 ? 4 : (NCB + 2 * MAXS) <= 4 ? (CPLX ? (sizeof(R) == 8 ? 4 : 5) : 8)
                                                     : (CPLX ? 4 : (sizeof(R) == 8 ? 5 : 6));
     v4 acc[MAXS][2][NCB], aci[MAXS][2][NCB];
     // column of register r of column tile cb (lane group g)
@@ -552,52 +552,54 @@ struct PanelGemm {
                 buf_store<T>(rs, row + 1 < n && colok ? off(row + 1, kp + col) : kBufOOB, T(v1));
             }
         };
-        // one 32-column half: x[cp][e] = P(half) W^T from the accumulator tiles 2 h, 2 h + 1
-        auto half = [&](auto hh, const T* wmh, v4 (&x)[2][2]) __attribute__((always_inline)) {
-            constexpr int h = hh;
-            static_for<0, 2>([&](auto pp) {
-                constexpr int cp = pp;
-                static_for<0, 2>([&](auto ee) { x[cp][ee] = v4{R(0), R(0), R(0), R(0)}; });
-                static_for<0, 4>([&](auto rr) {
-                    static_for<0, 2>([&](auto cc) {
-                        constexpr int r = rr, cb = cc;
-                        if constexpr (!(cp == 0 && 2 * M::row(r, 0) + cb >= 16)) {
-                            const int c = 2 * M::row(r, g) + cb;
-                            const T a = wmh[(16 * cp + l16) * LDD + c];
-                            static_for<0, 2>([&](auto ee) {
-                                constexpr int e = ee;
-                                x[cp][e] = M::mac(a, acc[0][e][2 * h + cb][r], x[cp][e]);
-                            });
-                        }
-                    });
-                });
-                static_for<0, 4>([&](auto rr) {
-                    constexpr int r = rr;
-                    const int col = 16 * cp + M::row(r, g);
-                    const R d0 = x[cp][0][r], d1 = x[cp][1][r];
-                    store_pair(32 * h + col, 32 * h + col < w, d0, d1);
+        // 16 columns 16 cp.. of half h: x[e] = P(half) W^T from the
+        // accumulator tiles 2 h, 2 h + 1, stored
+        auto part = [&](auto hh, auto pp, const T* wmh, v4 (&x)[2]) __attribute__((always_inline)) {
+            constexpr int h = hh, cp = pp;
+            static_for<0, 2>([&](auto ee) { x[ee] = v4{R(0), R(0), R(0), R(0)}; });
+            static_for<0, 4>([&](auto rr) {
+                static_for<0, 2>([&](auto cc) {
+                    constexpr int r = rr, cb = cc;
+                    if constexpr (!(cp == 0 && 2 * M::row(r, 0) + cb >= 16)) {
+                        const int c = 2 * M::row(r, g) + cb;
+                        const T a = wmh[(16 * cp + l16) * LDD + c];
+                        static_for<0, 2>([&](auto ee) {
+                            constexpr int e = ee;
+                            x[e] = M::mac(a, acc[0][e][2 * h + cb][r], x[e]);
+                        });
+                    }
                 });
             });
-        };
-        v4 xa[2][2];
-        half(ic<0>{}, wm1, xa);
-        // P_b -= L_a L21'^T
-        static_for<0, 2>([&](auto pp) {
             static_for<0, 4>([&](auto rr) {
-                constexpr int cp = pp, r = rr;
+                constexpr int r = rr;
+                const int col = 16 * cp + M::row(r, g);
+                const R d0 = x[0][r], d1 = x[1][r];
+                store_pair(32 * h + col, 32 * h + col < w, d0, d1);
+            });
+        };
+        // the first half, each 16-column group applied to P_b as soon as it
+        // is solved: P_b -= L_a(:, group) L21'(:, group)^T
+        static_for<0, 2>([&](auto pp) {
+            constexpr int cp = pp;
+            v4 x[2];
+            part(ic<0>{}, ic<cp>{}, wm1, x);
+            static_for<0, 4>([&](auto rr) {
+                constexpr int r = rr;
                 const int cpr = 16 * cp + M::row(r, g);
                 static_for<0, 2>([&](auto cc) {
                     constexpr int cb = cc;
                     const T a = -pl[(2 * l16 + cb) * LDD + cpr];
                     static_for<0, 2>([&](auto ee) {
                         constexpr int e = ee;
-                        acc[0][e][2 + cb] = M::mac(a, xa[cp][e][r], acc[0][e][2 + cb]);
+                        acc[0][e][2 + cb] = M::mac(a, x[e][r], acc[0][e][2 + cb]);
                     });
                 });
             });
         });
-        v4 xb[2][2];
-        half(ic<1>{}, wm2, xb);
+        static_for<0, 2>([&](auto pp) {
+            v4 x[2];
+            part(ic<1>{}, pp, wm2, x);
+        });
     }
 };
 
@@ -713,9 +715,10 @@ __device__ __forceinline__ void factor_matrix(__amdgpu_buffer_rsrc_t rs, uint32_
 //   wave 0:     factor P11 (L11, W1); L21' = P21' W1^T on MFMA (to the
 //               matrix and to pl); P22 -= L21' L21'^T on MFMA; factor P22
 //               (L22, W2)
-//   waves 1..3: GEMM of superblocks 2..4, kept in the accumulators
+//   waves 1..3: GEMM of superblocks w + 1 and w + 4, kept in the
+//               accumulators
 //   sync
-//   waves 1..3: solve the kept superblock from the accumulators in two
+//   waves 1..3: solve the kept superblocks from the accumulators in two
 //               stages (solve_store2)
 //   all waves:  the remaining superblocks, round-robin: GEMM, two-stage solve
 //   sync
@@ -760,9 +763,9 @@ __device__ __forceinline__ void factor_matrix_wide(__amdgpu_buffer_rsrc_t rs, ui
         gd.template accumulate<true>(0, q1);
         gd.finish_lds(dst, w);
     };
-    // the superblocks from 5 on, round-robin over the four waves
+    // the superblocks from 8 on, round-robin over the four waves
     auto rest = [&](int k, int w, int RS) __attribute__((always_inline)) {
-        for (int sb = 5 + wave; sb < RS; sb += WAVES) {
+        for (int sb = 8 + wave; sb < RS; sb += WAVES) {
             G64 gm;
             setup(gm, k, RS, sb);
             gm.begin(w);
@@ -840,15 +843,21 @@ __device__ __forceinline__ void factor_matrix_wide(__amdgpu_buffer_rsrc_t rs, ui
             }
             __syncthreads();
             {
-                G64 gm;
+                G64 gm, gn;
                 setup(gm, k, RS, wave + 1);
-                const bool mine = wave + 1 < RS;
+                setup(gn, k, RS, wave + 4);
+                const bool mine = wave + 1 < RS, next = wave + 4 < RS;
                 if (mine) {
                     gm.begin(w);
                     gm.template accumulate<true>(0, k);
                 }
+                if (next) {
+                    gn.begin(w);
+                    gn.template accumulate<true>(0, k);
+                }
                 __syncthreads();
                 if (mine) gm.solve_store2(wm1, wm2, pl, w);
+                if (next) gn.solve_store2(wm1, wm2, pl, w);
             }
             rest(k, w, RS);
             __syncthreads();
