@@ -188,32 +188,64 @@ __device__ __forceinline__ void factor_diag(T* pb, T* wm, double* colx, double* 
     });
     rdiag[i] = rsd_mine;
     wave_lds_sync();
-    // Inverse: lane i forms column i of W = L11^-1 by forward substitution,
-    //     W(m, i) = (delta(m, i) - sum_{p < m} L(m, p) W(p, i)) / L(m, m),
-    // from the stored factor (as the solve will use it); columns are
-    // independent, so no exchange between lanes is needed.  Row m of L11 is
-    // read in one batch while row m - 1 is summed, and the sum runs as four
-    // interleaved partial sums.
-    const uint32_t pbo = lds_offset(pb);
-    double x[NBP];
-    double lr[2][NBP];   // row m in lr[m & 1], row m + 1 arriving in the other
-    static_for<0, NBP>([&](auto mm) {
-        constexpr int m = mm;
-        if constexpr (m + 1 < NBP) {
-            const lds_cptr<T> row = lds_after<T>(pbo + uint32_t((m + 1) * LDD) * uint32_t(sizeof(T)),
-                                                 x[m > 0 ? m - 1 : 0]);
-            static_for<0, m + 1>([&](auto pp) { lr[(m + 1) & 1][pp] = double(row[pp]); });
-        }
-        const double rd = rdiag[m];
-        __builtin_amdgcn_sched_barrier(0);
-        double acc[4] = {(m == i) ? 1.0 : 0.0, 0.0, 0.0, 0.0};
-        static_for<0, m>([&](auto pp) {
-            constexpr int p = pp;
-            acc[p & 3] = __builtin_fma(-lr[m & 1][p], x[p], acc[p & 3]);
+    // Inverse W = L11^-1 in 16 x 16 blocks.  The diagonal blocks W11 and W22
+    // (inverses of the diagonal blocks of L11) by forward substitution,
+    //     W(m, c) = (delta(m, c) - sum_{p < m} L(m, p) W(p, c)) / L(m, m),
+    // lane i forming column i mod 16 of block i / 16, both blocks at once (a
+    // chain of 16 rows instead of 32); row m + 1 of the block is read in one
+    // batch while row m is summed, the sum running as four interleaved
+    // partial sums.  Then W21 = -W22 (L21 W11) as two 16 x 16 x 16 MFMA
+    // products, the first one's result registers feeding the second as its B
+    // operand (register r of lane group g holds row row(r, g) of L21 W11, four
+    // distinct rows over the groups).  W12 = 0.
+    {
+        const int blk = i >> 4, ci = i & 15;
+        const uint32_t pbo = lds_offset(pb) + uint32_t(16 * blk * (LDD + 1)) * uint32_t(sizeof(T));
+        double x[16];
+        double lr[2][16];   // row m in lr[m & 1], row m + 1 arriving in the other
+        static_for<0, 16>([&](auto mm) {
+            constexpr int m = mm;
+            if constexpr (m + 1 < 16) {
+                const lds_cptr<T> row = lds_after<T>(pbo + uint32_t((m + 1) * LDD) * uint32_t(sizeof(T)),
+                                                     x[m > 0 ? m - 1 : 0]);
+                static_for<0, m + 1>([&](auto pp) { lr[(m + 1) & 1][pp] = double(row[pp]); });
+            }
+            const double rd = rdiag[16 * blk + m];
+            __builtin_amdgcn_sched_barrier(0);
+            double acc[4] = {(m == ci) ? 1.0 : 0.0, 0.0, 0.0, 0.0};
+            static_for<0, m>([&](auto pp) {
+                constexpr int p = pp;
+                acc[p & 3] = __builtin_fma(-lr[m & 1][p], x[p], acc[p & 3]);
+            });
+            x[m] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * rd;
         });
-        x[m] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * rd;
-    });
-    static_for<0, NBP>([&](auto mm) { wm[mm * LDD + i] = T(x[mm]); });
+        static_for<0, 16>([&](auto mm) {
+            constexpr int m = mm;
+            wm[(16 * blk + m) * LDD + 16 * blk + ci] = T(x[m]);
+        });
+        if (blk == 1) static_for<0, 16>([&](auto mm) { wm[mm * LDD + 16 + ci] = T(0); });   // W12
+
+    }
+    wave_lds_sync();
+    {
+        using MD = Mfma<double>;
+        const int l16 = lane & 15, g = (lane >> 4) & 3;
+        typename MD::v4 t = {0.0, 0.0, 0.0, 0.0}, y = {0.0, 0.0, 0.0, 0.0};
+        static_for<0, 4>([&](auto uu) {        // t = L21 W11
+            constexpr int u = uu;
+            t = MD::mac(double(pb[(16 + l16) * LDD + 4 * u + g]), double(wm[(4 * u + g) * LDD + l16]), t);
+        });
+        static_for<0, 4>([&](auto rr) {        // y = W22 t
+            constexpr int r = rr;
+            const double tr = t[r];
+            y = MD::mac(double(wm[(16 + l16) * LDD + 16 + MD::row(r, g)]), tr, y);
+        });
+        static_for<0, 4>([&](auto rr) {
+            constexpr int r = rr;
+            const double yr = y[r];
+            wm[(16 + MD::row(r, g)) * LDD + l16] = T(-yr);
+        });
+    }
     if (lane == 0) s_inf = inf;
 }
 
