@@ -752,13 +752,14 @@ __device__ __forceinline__ void factor_matrix(__amdgpu_buffer_rsrc_t rs, uint32_
 //   sync
 //   waves 1..3: solve the kept superblocks from the accumulators in two
 //               stages (solve_store2)
-//   all waves:  the remaining superblocks, round-robin: GEMM, two-stage solve
+//   all waves:  the remaining superblocks, each taken by the next wave free:
+//               GEMM, two-stage solve
 //   sync
 template <typename T, bool UPPER, bool PAIRED>
 __device__ __forceinline__ void factor_matrix_wide(__amdgpu_buffer_rsrc_t rs, uint32_t ld, int n,
                                                    int wave, T* p11, T* wm1, T* pa, T* p22, T* pl,
                                                    T* wm2, double* colx, double* rdiag,
-                                                   int32_t* s_inf)
+                                                   int32_t* s_inf, int32_t* ctr)
 {
     using R = typename Traits<T>::R;
     using M = Mfma<R>;
@@ -795,9 +796,15 @@ __device__ __forceinline__ void factor_matrix_wide(__amdgpu_buffer_rsrc_t rs, ui
         gd.template accumulate<true>(0, q1);
         gd.finish_lds(dst, w);
     };
-    // the superblocks from 8 on, round-robin over the four waves
+    // the superblocks from 8 on, each taken by the next wave free (the waves
+    // that solve kept superblocks first come later): an LDS counter, reset by
+    // wave 0 between the syncs before this phase
     auto rest = [&](int k, int w, int RS) __attribute__((always_inline)) {
-        for (int sb = 8 + wave; sb < RS; sb += WAVES) {
+        for (;;) {
+            int j = 0;
+            if (lane_now() == 0) j = atomicAdd(ctr, 1);
+            const int sb = 8 + __builtin_amdgcn_readlane(j, 0);
+            if (sb >= RS) break;
             G64 gm;
             setup(gm, k, RS, sb);
             gm.begin(w);
@@ -813,6 +820,7 @@ __device__ __forceinline__ void factor_matrix_wide(__amdgpu_buffer_rsrc_t rs, ui
             const int wa = min(NBP, w), wb = w - NBP;    // wb <= 0: no second half
             const int RS = (n - k + 31) >> 5;
             __syncthreads();
+            if (lane_now() == 0) *ctr = 0;
             factor_diag<T, UPPER>(p11, wm1, colx, rdiag, lane_now(), k, n, wa, rs, ld, *s_inf);
             if (wb > 0) {
                 wave_lds_sync();
@@ -910,6 +918,7 @@ struct Smem {
     C colx[2 * NBP];
     Rc rdiag[NBP];
     int32_t inf;
+    int32_t ctr;   // superblocks taken (64-column panels)
 };
 
 template <typename T, bool UPPER>
@@ -933,13 +942,13 @@ void potrf_blocked_kernel(T* __restrict__ A, int n, int64_t lda, int64_t stride,
         } else if constexpr (!UPPER && sizeof(R) == 8) {
             if ((n & 1) == 0)
                 factor_matrix_wide<T, UPPER, true>(rs, ld, n, wave, sm.p11, sm.wm, sm.pa, sm.p22, sm.pl, sm.wm2,
-                                                   sm.colx, sm.rdiag, &sm.inf);
+                                                   sm.colx, sm.rdiag, &sm.inf, &sm.ctr);
             else
                 factor_matrix_wide<T, UPPER, false>(rs, ld, n, wave, sm.p11, sm.wm, sm.pa, sm.p22, sm.pl, sm.wm2,
-                                                    sm.colx, sm.rdiag, &sm.inf);
+                                                    sm.colx, sm.rdiag, &sm.inf, &sm.ctr);
         } else {
             factor_matrix_wide<T, UPPER, false>(rs, ld, n, wave, sm.p11, sm.wm, sm.pa, sm.p22, sm.pl, sm.wm2,
-                                                sm.colx, sm.rdiag, &sm.inf);
+                                                sm.colx, sm.rdiag, &sm.inf, &sm.ctr);
         }
         if (threadIdx.x == 0 && info != nullptr) info[b] = sm.inf;
         __syncthreads();
