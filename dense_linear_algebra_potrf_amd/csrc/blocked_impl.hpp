@@ -161,9 +161,12 @@ __device__ __forceinline__ void factor_diag(T* pb, T* wm, double* colx, double* 
         }
         __builtin_amdgcn_sched_barrier(0);
         if (j < w) inf = (inf == 0 && !(d > 0.0)) ? (k + j + 1) : inf;
+        // the multiplier S(i, j) / d from the reciprocal of d, the shorter
+        // dependent chain; sqrt(d) and 1/sqrt(d), for column j itself, run
+        // beside it
         double sq, rsd;
         pivot_sqrt_rsq(d, sq, rsd);
-        const double beta = v[j] * (rsd * rsd);       // S(i, j) / d
+        const double beta = v[j] * pivot_rcp(d);
         // rows at or above j only touch slots right of the diagonal (unused)
         if constexpr (j + 1 < NBP) {
             v[j + 1] = __builtin_fma(-beta, s1, v[j + 1]);
