@@ -98,21 +98,20 @@ template <typename V, typename D> __device__ __forceinline__ lds_cptr<V> lds_aft
     return (lds_cptr<V>)uintptr_t(off);
 }
 
-// The diagonal block of a panel (real types), factored in double by one
+// A 32 x 32 diagonal block (real types), factored in double by one
 // wavefront.  Lane i (i = lane mod 32; the upper half of the wave repeats the
-// lower half) holds row i of the block.  At step j the Schur pivot d = S(j, j)
-// is read from the published column (a lane read into scalar registers was
-// tried: the scalar pressure made the kernel spill), rows below j take the
-// Schur update of their entries right of column j with
-// the multiplier S(i, j) / d, and column j is scaled by 1/sqrt(d) (the
-// diagonal becomes sqrt(d)).  Column j + 1 is updated first and published to
-// LDS at once, so the exchange overlaps the rest of the step's updates.  Rows
-// at or beyond n are the identity.  The factor goes to the matrix and to the
-// first rows of the panel buffer, 1/L(j, j) to rdiag, and the inverse W of
-// the factor (below) to wm for the solve of the rows below.  Every LDS store is unconditional (the two
-// halves of the wave write identical values): stores under a lane condition
-// split the code into many small blocks, after which the compiler keeps
-// hundreds of values live and spills.
+// lower half) holds row i of the block.  At step j the pivot d = S(j, j) and
+// S(j + 1, j) are read from lanes j and j + 1 directly (lane reads), rows
+// below j take the Schur update of their entries right of column j with the
+// multiplier S(i, j) / d, and column j is scaled by 1/sqrt(d) (the diagonal
+// becomes sqrt(d)).  Column j + 1 is updated first and published to LDS, from
+// where the other lanes read it in one batch at the next step, off the chain
+// of dependent pivots.  Rows at or beyond n are the identity.  The factor goes
+// to the matrix and back into the block buffer pb, 1/L(j, j) to rdiag, and the
+// inverse W of the factor (below) to wm for the solves.  The LDS stores of the
+// step loop are unconditional (the two halves of the wave write identical
+// values): stores under a lane condition split the code into many small
+// blocks, after which the compiler keeps hundreds of values live and spills.
 template <typename T, bool UPPER>
 __device__ __forceinline__ void factor_diag(T* pb, T* wm, double* colx, double* rdiag,
                                             int lane, int k, int n, int w,
@@ -180,7 +179,7 @@ __device__ __forceinline__ void factor_diag(T* pb, T* wm, double* colx, double* 
         rsd_mine = (i == j) ? rsd : rsd_mine;
         wave_lds_sync();
     });
-    // the factor: to the matrix, and into the first rows of the panel buffer
+    // the factor: to the matrix, and back into the block buffer
     static_for<0, NBP>([&](auto cc) {
         constexpr int c = cc;
         const bool st = writer && c <= i && c < w && !pad;
@@ -972,7 +971,7 @@ bool geometry_t(int n, int64_t batch, Geometry& g) {
     g.family = FAM_BLOCKED;
     g.P = g.R = g.G = 0;
     g.threads = 64 * WAVES;
-    g.panel = NBP;
+    g.panel = Traits<T>::cplx ? NBP : 2 * NBP;   // real types: 64-column panels
     g.grid = batch < kMaxGrid ? batch : kMaxGrid;
     g.lds = int64_t(sizeof(Smem<T>));
     return true;
