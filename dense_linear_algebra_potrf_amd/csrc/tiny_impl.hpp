@@ -193,10 +193,22 @@ __device__ __forceinline__ void factor_rows(T (&a)[R][P * R], typename Traits<T>
     static_for<0, R>([&](auto rr) { invd[rr] = Rt(1); });
     publish(ic<0>{});
     wave_lds_sync();
+    // With one matrix per wavefront (P = 64, R = 1) lane i holds row i, and
+    // the pivot and the entry S(j + 1, j) that the next pivot's chain needs
+    // are read from lanes j and j + 1 directly, without the LDS round trip.
+    constexpr bool LANE_READ = P == 64 && R == 1;
+    auto lane_read = [](const T& x, int src) __attribute__((always_inline)) {
+        uint32_t w[words<T>()];
+        __builtin_memcpy(w, &x, sizeof(T));
+        static_for<0, words<T>()>([&](auto ii) { w[ii] = __builtin_amdgcn_readlane(w[ii], src); });
+        T y;
+        __builtin_memcpy(&y, w, sizeof(T));
+        return y;
+    };
     static_for<0, NB>([&](auto jj) {
         constexpr int j = jj;
         constexpr int rj = j / P;
-        const Rt d = re(colv(j, j));
+        const Rt d = LANE_READ ? re(lane_read(a[0][j], j)) : re(colv(j, j));
         inf = (inf == 0 && !(d > Rt(0))) ? (j + 1) : inf;
         const Rt inv = pivot_rcp(d);
         const Rt rs = pivot_rsq(d);
@@ -207,7 +219,7 @@ __device__ __forceinline__ void factor_rows(T (&a)[R][P * R], typename Traits<T>
         });
         if constexpr (j + 1 < NB) {
             constexpr int rn = (j + 1) / P;
-            const T cj1 = colv(j, j + 1);
+            const T cj1 = LANE_READ ? lane_read(a[0][j], j + 1) : colv(j, j + 1);
             static_for<rn, R>([&](auto rr) {
                 constexpr int r = rr;
                 sub_mul_conj(a[r][j + 1], t[r], cj1);
