@@ -8,29 +8,34 @@
 // workgroup of four wavefronts runs the panels of one matrix itself,
 // left-looking:
 //
-//   for each panel of NBP = 32 columns starting at k:
-//     (i)   GEMM: P = S(k:n, k:k+32) - L(k:n, 0:k) L(k:k+32, 0:k)^T on MFMA
+//   for each panel starting at column k:
+//     (i)   GEMM: P = S(k:n, k:k+w) - L(k:n, 0:k) L(k:k+w, 0:k)^T on MFMA
 //           (v_mfma_*_16x16x4, accumulated as L L^T - S so that no operand needs
-//           negating).  Wave 0 computes the 32 x 32 diagonal block into LDS,
-//           the other waves the 32-row superblocks below it, in registers;
-//     (ii)  meanwhile wave 0 factors the diagonal block and forms the inverse
-//           W of its factor column by column, info merged as k + j + 1;
+//           negating): the diagonal block into LDS, the 32-row superblocks
+//           below it in registers;
+//     (ii)  one wave factors the diagonal block in 32 x 32 blocks and forms the
+//           inverse W of each factor, info merged as k + j + 1, while the
+//           other waves run their GEMMs;
 //     (iii) the rows below are solved by a second MFMA product
 //           L21 = P21 W^T (W lower triangular, zero blocks skipped) straight
 //           from the GEMM's accumulators, and L21 is written over S, where
 //           the next panels read it.
-//   Only the diagonal block, W and a few vectors live in LDS, so two
-//   workgroups (matrices) share a compute unit: while one factors its
-//   diagonal block on one wave, the other keeps the matrix cores busy.
+//   The real types take 64-column panels (the left-looking GEMM re-reads
+//   the columns of L left of k once per panel, so the wider panel halves
+//   that traffic; factor_matrix_wide), the complex types 32-column ones
+//   (factor_matrix).  Only the diagonal blocks, their inverses and a few
+//   vectors live in LDS, so two workgroups (matrices) share a compute unit:
+//   while one factors a diagonal block on one wave, the other keeps the
+//   matrix cores busy.
 //
 // S = A for Lower, S(i, c) = conj(A(c, i)) for Upper; for the real types the
-// Upper form only swaps the address of each element.  The complex types run
-// the same schedule with each complex product split into four real MFMAs on
-// separate real and imaginary accumulators (the pages' complex trailing update
-// is a ConjTrans GEMM).  Only the referenced
-// triangle is read or written; rows beyond n load as zero and are never
-// stored.  Failure handling follows the pages' info contract: the first
-// failing pivot column is kept; later work runs on with NaN.
+// Upper form only swaps the address of each element.  The complex types
+// split each complex product into four real MFMAs on separate real and
+// imaginary accumulators (the pages' complex trailing update is a ConjTrans
+// GEMM).  Only the referenced triangle is read or written; rows beyond n load
+// as zero and are never stored.  Failure handling follows the pages' info
+// contract: the first failing pivot column is kept; the columns before it are
+// final, and the rest is not meaningful.
 #pragma once
 
 #include "families.hpp"
