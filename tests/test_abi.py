@@ -175,3 +175,25 @@ def test_no_kernel_uses_scratch(lib):
     bad = {k: v for k, v in res.items()
            if v.get("scratch_bytes", 0) != 0 and not allowed(k, v["scratch_bytes"])}
     assert not bad, f"kernels with scratch (dynamic register indexing?): {sorted(bad)}"
+
+
+def test_counter_digest_follows_the_family_sources(tmp_path, monkeypatch):
+    """A committed counter run stays attached while its kernel family's sources
+    are unchanged: a change elsewhere (another family) keeps the digest, a change
+    in the family's own file or a shared header moves it."""
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    csrc = tmp_path / "dense_linear_algebra_potrf_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for name in ("tiny_impl.hpp", "blocked_impl.hpp", "common.hpp", "api.cpp"):
+        (csrc / name).write_text(name)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    tiny0, all0 = bench.source_digest("tiny"), bench.source_digest()
+    (csrc / "blocked_impl.hpp").write_text("changed")
+    assert bench.source_digest("tiny") == tiny0
+    assert bench.source_digest() != all0
+    (csrc / "tiny_impl.hpp").write_text("changed")
+    tiny1 = bench.source_digest("tiny")
+    assert tiny1 != tiny0
+    (csrc / "common.hpp").write_text("changed")
+    assert bench.source_digest("tiny") != tiny1
