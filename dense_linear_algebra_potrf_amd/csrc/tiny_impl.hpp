@@ -32,7 +32,11 @@
 namespace bl {
 namespace tiny_detail {
 
-constexpr int kTinyWaves = 4;   // wavefronts per workgroup, each independent
+// Wavefronts per workgroup (each independent).  One: a finished wavefront's
+// slot takes the next workgroup at once, where a wider workgroup would hold its
+// slots until its slowest wavefront ends (at one wavefront per SIMD, the 64 x 1
+// window ran 15% slower with four per workgroup).
+constexpr int kTinyWaves = 1;
 
 // Dwords per partition row of the column buffer: >= nb * D, of the form
 // 32 m + 4, so partitions of a wave start on different 16-byte bank groups.
