@@ -106,7 +106,7 @@ const char* dtype_name(DT dt) {
 // beyond.  Values come from measurements of both families on MI355X.
 int auto_tiny_cut(DT dt) {
     switch (dt) {
-    case DT::F32: return 33;
+    case DT::F32: return 64;    // the 64 x 1 window: 184 us against 392 at n=48 (b16384)
     case DT::F64: return 32;
     case DT::C64: return 64;    // the 64 x 1 window beats the LDS family at 33..64
     case DT::C128: return 16;
