@@ -107,9 +107,9 @@ const char* dtype_name(DT dt) {
 int auto_tiny_cut(DT dt) {
     switch (dt) {
     case DT::F32: return 64;    // the 64 x 1 window: 184 us against 392 at n=48 (b16384)
-    case DT::F64: return 32;
+    case DT::F64: return 64;    // 64 x 1: 324 us against 438 at n=33, 342 against 2593 at n=64
     case DT::C64: return 64;    // the 64 x 1 window beats the LDS family at 33..64
-    case DT::C128: return 16;
+    case DT::C128: return 32;   // 32 x 1: 90-115 us against 321-993 at n=17..32
     }
     return 0;
 }

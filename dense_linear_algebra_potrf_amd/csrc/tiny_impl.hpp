@@ -459,12 +459,25 @@ __global__ __launch_bounds__(PACKED ? 64 : 64 * kTinyWaves) void potrf_tiny_kern
             buf_store<T>(rsrc, masked(uint32_t(e) * S, ok), lds_get<T>(xbuf, idx));
         }, std::true_type{});
     } else {
+        // With one matrix per wavefront the row fills most of the registers:
+        // the row offset and index are hidden from the optimiser here, so that
+        // the stores recompute their per-column offsets and masks instead of
+        // keeping the loads' ones live across the factorisation (which leaves
+        // the factor loop one staging register for its LDS reads).
+        uint32_t roff_st[R];
+        int q_st = q;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            roff_st[r] = roff[r];
+            if constexpr (P == 64) asm volatile("" : "+v"(roff_st[r]));
+        }
+        if constexpr (P == 64) asm volatile("" : "+v"(q_st));
         static_for<0, R>([&](auto rr) {
             constexpr int r = rr;
-            const int i = q + r * P;
+            const int i = q_st + r * P;
             static_for<0, cmin(NB, (r + 1) * P)>([&](auto cc) {
                 constexpr int c = cc;
-                uint32_t off = UPPER ? elem_off(r, c) : roff[r];
+                uint32_t off = UPPER ? roff_st[r] + uint32_t(c) * S : roff_st[r];
                 if constexpr (c >= r * P) off = (c <= i) ? off : kBufOOB;
                 if constexpr (UPPER) buf_store<T>(rsrc, off, conj(a[r][c]));
                 else buf_store<T>(rsrc, off, a[r][c], uint32_t(c) * lda_b);
@@ -492,13 +505,13 @@ template <> struct TinyConfigs<float> {
                        TC<16, 2>, TC<11, 3, 4>, TC<64, 1>>;
 };
 template <> struct TinyConfigs<double> {
-    using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<8, 3>, TC<8, 4>>;
+    using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<8, 3>, TC<8, 4>, TC<64, 1>>;
 };
 template <> struct TinyConfigs<cfloat> {
     using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<8, 3>, TC<8, 4>, TC<64, 1>>;
 };
 template <> struct TinyConfigs<cdouble> {
-    using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>>;
+    using type = TList<TC<4, 1>, TC<8, 1>, TC<6, 2>, TC<8, 2>, TC<32, 1>>;
 };
 
 // posv keeps more per lane (both solves' right-hand sides): smaller windows for

@@ -117,6 +117,10 @@ def test_route_auto_picks_by_size(lib):
     assert bl.route("f32", "L", 8, 1024)["family"] == "tiny"
     assert bl.route("f32", "L", 17, 32768)["family"] == "tiny"
     assert bl.route("c128", "U", 16, 64)["family"] == "tiny"
+    # the one-matrix-per-wavefront windows end each type's tiny range
+    for dt, top in (("f32", 64), ("f64", 64), ("c64", 64), ("c128", 32)):
+        assert bl.route(dt, "L", top, 16384)["family"] == "tiny"
+        assert bl.route(dt, "U", top + 1, 16384)["family"] == "lds"
     # above the LDS family's capacity the complex types go to the blocked family
     assert bl.route("c64", "U", 128, 64)["family"] == "blocked"
     assert bl.route("c64", "L", 512, 64)["family"] == "blocked"
