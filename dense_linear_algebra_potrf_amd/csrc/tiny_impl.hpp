@@ -150,6 +150,17 @@ __device__ __forceinline__ void tiny_solves(const T (&a)[R][P * R], const typena
     });
 }
 
+// x as held by lane src (src wave-uniform)
+template <typename T>
+__device__ __forceinline__ T lane_read(const T& x, int src) {
+    uint32_t w[words<T>()];
+    __builtin_memcpy(w, &x, sizeof(T));
+    static_for<0, words<T>()>([&](auto ii) { w[ii] = __builtin_amdgcn_readlane(w[ii], src); });
+    T y;
+    __builtin_memcpy(&y, w, sizeof(T));
+    return y;
+}
+
 // The column recurrence on the rows a lane holds (rows i = q + r P of the
 // matrix of partition p), with the pivot columns exchanged through xbuf
 // (two parity buffers of PARTS rows of ROWW words).  On return a holds the
@@ -197,22 +208,10 @@ __device__ __forceinline__ void factor_rows(T (&a)[R][P * R], typename Traits<T>
     static_for<0, R>([&](auto rr) { invd[rr] = Rt(1); });
     publish(ic<0>{});
     wave_lds_sync();
-    // With one matrix per wavefront (P = 64, R = 1) lane i holds row i, and
-    // the pivot and the entry S(j + 1, j) that the next pivot's chain needs
-    // are read from lanes j and j + 1 directly, without the LDS round trip.
-    constexpr bool LANE_READ = P == 64 && R == 1;
-    auto lane_read = [](const T& x, int src) __attribute__((always_inline)) {
-        uint32_t w[words<T>()];
-        __builtin_memcpy(w, &x, sizeof(T));
-        static_for<0, words<T>()>([&](auto ii) { w[ii] = __builtin_amdgcn_readlane(w[ii], src); });
-        T y;
-        __builtin_memcpy(&y, w, sizeof(T));
-        return y;
-    };
     static_for<0, NB>([&](auto jj) {
         constexpr int j = jj;
         constexpr int rj = j / P;
-        const Rt d = LANE_READ ? re(lane_read(a[0][j], j)) : re(colv(j, j));
+        const Rt d = re(colv(j, j));
         inf = (inf == 0 && !(d > Rt(0))) ? (j + 1) : inf;
         const Rt inv = pivot_rcp(d);
         const Rt rs = pivot_rsq(d);
@@ -223,7 +222,7 @@ __device__ __forceinline__ void factor_rows(T (&a)[R][P * R], typename Traits<T>
         });
         if constexpr (j + 1 < NB) {
             constexpr int rn = (j + 1) / P;
-            const T cj1 = LANE_READ ? lane_read(a[0][j], j + 1) : colv(j, j + 1);
+            const T cj1 = colv(j, j + 1);
             static_for<rn, R>([&](auto rr) {
                 constexpr int r = rr;
                 sub_mul_conj(a[r][j + 1], t[r], cj1);
@@ -249,6 +248,93 @@ __device__ __forceinline__ void factor_rows(T (&a)[R][P * R], typename Traits<T>
         });
     });
 
+}
+
+// The same recurrence with one matrix per wavefront (P = 64, R = 1: lane i
+// holds row i), arranged so that its latencies overlap.  The pivot and the
+// entry S(j + 1, j) are read from lanes j and j + 1 directly, without the LDS
+// round trip.  Step j + 1's pivot,
+// reciprocals and scaled entries are computed in step j, as soon as column
+// j + 1 is final.  The broadcast reads of the published column go in chunks of
+// 64 bytes, each issued one chunk ahead of the updates that use it, with
+// scheduling fences between chunks: left to itself the scheduler issues each
+// read just before its use and then waits for it, one LDS round trip per
+// read.  The exchange buffer layout and the scratch slots are those of
+// factor_rows.
+template <typename T, bool UPPER, int NRHS, int ROWW>
+__device__ __forceinline__ void factor_rows_lane(T (&a)[1][64], typename Traits<T>::R (&invd)[1],
+                                                 uint32_t* xbuf, int q, int32_t& inf)
+{
+    using Rt = typename Traits<T>::R;
+    constexpr int NB = 64;
+    constexpr int CH = 64 / int(sizeof(T));     // column entries per chunk
+    auto xrow = [&](int par) -> uint32_t* { return xbuf + par * ROWW; };
+    auto publish = [&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        lds_put<T>(xrow(j & 1), q >= j ? q - j : NB, a[0][j]);
+    };
+
+    inf = 0;
+    invd[0] = Rt(1);
+    publish(ic<0>{});
+    wave_lds_sync();
+    Rt d = re(lane_read(a[0][0], 0));
+    Rt inv = pivot_rcp(d);
+    Rt rs = pivot_rsq(d);
+    T t = scale(a[0][0], inv);
+    static_for<0, NB>([&](auto jj) {
+        constexpr int j = jj;
+        // entries k = j + 2 .. NB - 1 of column j sit at slots s = k - j;
+        // chunk c holds slots [c CH, (c + 1) CH)
+        constexpr int NC = (NB - j + CH - 1) / CH;
+        constexpr bool BULK = j + 2 < NB;
+        const uint32_t* col = xrow(j & 1);
+        T cv[2][CH];
+        auto fetch = [&](auto cc) {
+            constexpr int c = cc;
+            static_for<cmax(2, c * CH), cmin((c + 1) * CH, NB - j)>([&](auto ss) {
+                constexpr int sl = ss;
+                cv[c & 1][sl - c * CH] = lds_get<T>(col, sl);
+            });
+        };
+        auto apply = [&](auto cc) {
+            constexpr int c = cc;
+            static_for<cmax(2, c * CH), cmin((c + 1) * CH, NB - j)>([&](auto ss) {
+                constexpr int sl = ss;
+                sub_mul_conj(a[0][j + sl], t, cv[c & 1][sl - c * CH]);
+            });
+        };
+        if constexpr (BULK) fetch(ic<0>{});
+        inf = (inf == 0 && !(d > Rt(0))) ? (j + 1) : inf;
+        Rt d_n = d, inv_n = inv, rs_n = rs;
+        T t_n = t;
+        if constexpr (j + 1 < NB) {
+            // column j + 1 first: it feeds the next pivot and the next exchange
+            sub_mul_conj(a[0][j + 1], t, lane_read(a[0][j], j + 1));
+            publish(ic<j + 1>{});
+            wave_lds_sync();
+            d_n = re(lane_read(a[0][j + 1], j + 1));
+            inv_n = pivot_rcp(d_n);
+            rs_n = pivot_rsq(d_n);
+            t_n = scale(a[0][j + 1], inv_n);
+        }
+        const bool diag = q == j;
+        a[0][j] = select(diag, diag_value<T>(pivot_sqrt(d), UPPER), scale(a[0][j], rs));
+        if constexpr (NRHS > 0) invd[0] = diag ? rs : invd[0];
+        if constexpr (BULK) {
+            static_for<0, NC>([&](auto cc) {
+                constexpr int c = cc;
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (c + 1 < NC) fetch(ic<c + 1>{});
+                apply(cc);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        d = d_n;
+        inv = inv_n;
+        rs = rs_n;
+        t = t_n;
+    });
 }
 
 // Packed path: each matrix's image in LDS starts at a multiple of IMGP
@@ -432,7 +518,10 @@ __global__ __launch_bounds__(PACKED ? 64 : 64 * kTinyWaves) void potrf_tiny_kern
 
     int32_t inf = 0;
     Rt invd[R];                 // 1 / L(i, i) of each held row (used by the solves)
-    factor_rows<T, P, R, UPPER, NRHS, ROWW>(a, invd, xbuf, p, q, inf);
+    if constexpr (P == 64 && R == 1)
+        factor_rows_lane<T, UPPER, NRHS, ROWW>(a, invd, xbuf, q, inf);
+    else
+        factor_rows<T, P, R, UPPER, NRHS, ROWW>(a, invd, xbuf, p, q, inf);
 
     if constexpr (NRHS > 0)
         tiny_solves<T, P, R, NRHS>(a, invd, xbuf, PARTS * ROWW, ROWW, p, q, live, n,
