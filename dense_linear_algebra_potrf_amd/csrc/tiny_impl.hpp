@@ -350,6 +350,21 @@ template <typename T, int P, int R>
 constexpr int packed_image_words() {
     return (63 / P + 2) * packed_pitch<P, R>() * words<T>();
 }
+// Upper with one matrix per wavefront (P = 64, R = 1, potrf): lane i's row is
+// column i of A, so per-row loads would have every instruction touch 64
+// cache lines, one element each, and with several wavefronts per CU the lines
+// leave the L1 cache before their other elements are read.  Instead the
+// matrix moves through LDS in slabs of SR rows of A, SR elements being one
+// 128-byte line of a column: lane l carries element (c0 + l mod SR,
+// u (64 / SR) + l / SR) of instruction u, so each instruction covers whole
+// lines, and the slab is transposed through a tile of 64 columns with a pitch
+// of one line plus 16 bytes.
+template <typename T, int P, int R, bool UPPER, int NRHS, bool PACKED>
+constexpr bool use_slabs() { return UPPER && P == 64 && R == 1 && NRHS == 0 && !PACKED; }
+template <typename T> constexpr int slab_rows() { return 128 / int(sizeof(T)); }
+template <typename T> constexpr int slab_pitch_words() { return slab_rows<T>() * words<T>() + 4; }
+template <typename T> constexpr int slab_tile_words() { return 64 * slab_pitch_words<T>(); }
+
 // Where the packed path is used (fp32 only), from timings of both variants on
 // MI355X over orders 8..33.  Lower: the rows of one column are contiguous,
 // so the per-row loads are already coalesced over a lane group, and the
@@ -391,7 +406,9 @@ __global__ __launch_bounds__(PACKED ? 64 : 64 * kTinyWaves) void potrf_tiny_kern
     constexpr int WAVES = PACKED ? 1 : kTinyWaves;
     constexpr int XW = 2 * PARTS * ROWW;                          // exchange words per wave
     constexpr int IMGW = PACKED ? packed_image_words<T, P, R>() : 0;
-    constexpr int LDSW = XW > IMGW ? XW : IMGW;
+    constexpr bool SLABS = use_slabs<T, P, R, UPPER, NRHS, PACKED>();
+    constexpr int SLABW = SLABS ? slab_tile_words<T>() : 0;
+    constexpr int LDSW = cmax(cmax(XW, IMGW), SLABW);
     __shared__ __attribute__((aligned(16))) uint32_t lds_raw[WAVES][LDSW];
 
     const int lane = threadIdx.x & 63;
@@ -480,6 +497,36 @@ __global__ __launch_bounds__(PACKED ? 64 : 64 * kTinyWaves) void potrf_tiny_kern
         }, std::false_type{});
         wave_lds_sync();
     }
+    if constexpr (SLABS) {
+        constexpr int SR = slab_rows<T>(), CPI = 64 / SR, SPW = slab_pitch_words<T>();
+        const int lr = lane % SR, lc = lane / SR;
+        // every load first (element (sb SR + lr, u CPI + lc) of A; only the
+        // referenced triangle of live columns is read, the rest comes back 0)
+        T st[64 / SR][SR];
+        static_for<0, 64 / SR>([&](auto sbc) {
+            constexpr int sb = sbc;
+            static_for<0, SR>([&](auto uc) {
+                constexpr int u = uc;
+                const int row = sb * SR + lr, col = u * CPI + lc;
+                const bool ok = live && col < n && row <= col;
+                st[sb][u] = buf_load<T>(rsrc, masked(uint32_t(col) * lda_b + uint32_t(row) * S, ok));
+            });
+        });
+        // then slab by slab through the tile: lane i takes column i's SR rows
+        static_for<0, 64 / SR>([&](auto sbc) {
+            constexpr int sb = sbc;
+            static_for<0, SR>([&](auto uc) {
+                constexpr int u = uc;
+                lds_put<T>(xbuf + (u * CPI + lc) * SPW, lr, st[sb][u]);
+            });
+            wave_lds_sync();
+            static_for<0, SR>([&](auto rc) {
+                constexpr int rr = rc;
+                a[0][sb * SR + rr] = lds_get<T>(xbuf + lane * SPW, rr);
+            });
+            wave_lds_sync();
+        });
+    } else
     static_for<0, R>([&](auto rr) {
         constexpr int r = rr;
         const int i = q + r * P;
@@ -547,6 +594,30 @@ __global__ __launch_bounds__(PACKED ? 64 : 64 * kTinyWaves) void potrf_tiny_kern
             const bool ok = (refbits[v / 32] >> (v % 32)) & 1u;
             buf_store<T>(rsrc, masked(uint32_t(e) * S, ok), lds_get<T>(xbuf, idx));
         }, std::true_type{});
+    } else if constexpr (SLABS) {
+        // the loads in reverse: lane i puts column i's SR rows of the slab in
+        // the tile, then each instruction stores whole lines of columns
+        constexpr int SR = slab_rows<T>(), CPI = 64 / SR, SPW = slab_pitch_words<T>();
+        int ln = lane;
+        asm volatile("" : "+v"(ln));     // offsets recomputed here, not kept from the loads
+        const int lr = ln % SR, lc = ln / SR;
+        wave_lds_sync();
+        static_for<0, 64 / SR>([&](auto sbc) {
+            constexpr int sb = sbc;
+            static_for<0, SR>([&](auto rc) {
+                constexpr int rr = rc;
+                lds_put<T>(xbuf + lane * SPW, rr, conj(a[0][sb * SR + rr]));
+            });
+            wave_lds_sync();
+            static_for<0, SR>([&](auto uc) {
+                constexpr int u = uc;
+                const int row = sb * SR + lr, col = u * CPI + lc;
+                const bool ok = live && col < n && row <= col;
+                buf_store<T>(rsrc, masked(uint32_t(col) * lda_b + uint32_t(row) * S, ok),
+                             lds_get<T>(xbuf + (u * CPI + lc) * SPW, lr));
+            });
+            wave_lds_sync();
+        });
     } else {
         // With one matrix per wavefront the row fills most of the registers:
         // the row offset and index are hidden from the optimiser here, so that
@@ -682,7 +753,8 @@ bool geometry_t(bool upper, int n, int64_t lda, int64_t stride, int64_t batch, G
         g.threads = 64 * waves;
         g.panel = 0;
         g.grid = (batch + gw * waves - 1) / (gw * waves);
-        g.lds = packed ? 4 * (xw > iw ? xw : iw) : int64_t(waves) * xw * 4;
+        const int64_t sw = (upper && C::P == 64 && C::R == 1 && !packed) ? slab_tile_words<T>() : 0;
+        g.lds = packed ? 4 * (xw > iw ? xw : iw) : int64_t(waves) * (xw > sw ? xw : sw) * 4;
     });
 }
 
