@@ -2,6 +2,8 @@
 CPU oracle on the same seeded inputs, and compare."""
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -14,6 +16,19 @@ from tests._checks import (RESIDUAL_BOUND, TOL, bits_equal, factor_residual, rel
 
 def announce(*parts):
     print("[case]", *parts, file=sys.stderr, flush=True)
+
+
+def record_error(kind: str, label: str, dt: str, uplo: str, n: int, batch: int, **errs):
+    """Print the observed worst-case errors of a parity case, and append them to
+    the JSON-lines file named by BATCHLAS_PARITY_LOG when that is set."""
+    vals = {k: float(v) for k, v in errs.items()}
+    print("[errors]", kind, label, dt, uplo, f"n={n}", f"batch={batch}",
+          " ".join(f"{k}={v:.3e}" for k, v in vals.items()), file=sys.stderr, flush=True)
+    path = os.environ.get("BATCHLAS_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(dict(kind=kind, label=label, dt=dt, uplo=uplo, n=n, batch=batch,
+                                    **vals)) + "\n")
 
 
 def torch_dtype(dt):
@@ -69,8 +84,11 @@ def check_potrf(a: np.ndarray, uplo: str, family: str = "auto", padded: bool = F
     if ok.size:
         err = rel_err_triangle(got, want, uplo, ok)
         worst = int(ok[np.argmax(err)])
-        assert err.max() <= tol, f"factor rel err {err.max():.3e} > {tol} (item {worst})"
         res = factor_residual(a, got, uplo, ok)
+        if label.startswith("config"):
+            record_error("potrf", label, dt, uplo, n, batch, factor_rel=err.max(),
+                         residual=res.max())
+        assert err.max() <= tol, f"factor rel err {err.max():.3e} > {tol} (item {worst})"
         assert res.max() <= RESIDUAL_BOUND, f"residual {res.max():.2f} > {RESIDUAL_BOUND}"
     # failed items: the leading info-1 columns are the leading block's factor
     for b in np.nonzero(info_ref > 0)[0][:64]:
@@ -115,9 +133,17 @@ def check_posv(a, b, uplo, family="auto", padded=False, label=""):
     far = syn.from_colmajor(aref, n, n, batch, lda, strideA)
     tol = TOL[dt]
     if ok.size:
-        assert rel_err_triangle(fa, far, uplo, ok).max() <= tol
-        assert rel_err(x, xr, ok).max() <= 10 * tol
-        assert solve_residual(a, x, b, ok).max() <= RESIDUAL_BOUND
+        ferr = rel_err_triangle(fa, far, uplo, ok).max()
+        xerr = rel_err(x, xr, ok).max()
+        sres = solve_residual(a, x, b, ok).max()
+        if label.startswith("config"):
+            record_error("posv", label, dt, uplo, n, batch, factor_rel=ferr, x_rel=xerr,
+                         residual=sres)
+        assert ferr <= tol, f"factor rel err {ferr:.3e} > {tol}"
+        # X at the same stated tolerance: with kappa(A) <= 5 the solves add about
+        # n u kappa (2e-5 at fp32 n = 32) to the factor's error
+        assert xerr <= tol, f"solution rel err {xerr:.3e} > {tol}"
+        assert sres <= RESIDUAL_BOUND, f"solve residual {sres:.2f} > {RESIDUAL_BOUND}"
     bad = np.nonzero(info_ref > 0)[0]
     if bad.size:
         assert bits_equal(x[bad], b[bad].astype(x.dtype)), "B changed for a failed item"

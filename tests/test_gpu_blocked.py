@@ -16,7 +16,7 @@ import pytest
 import oracle
 import synthetic as syn
 from tests._checks import RESIDUAL_BOUND, TOL, factor_residual, rel_err_triangle
-from tests._gpu import announce, check_potrf, gpu_potrf
+from tests._gpu import announce, check_potrf, gpu_potrf, record_error
 
 pytestmark = pytest.mark.gpu
 
@@ -86,7 +86,8 @@ def test_blocked_packed_batch_is_independent(dt):
 
 @pytest.mark.parametrize("planted", [False, True])
 def test_config_fp64_n512_b1024(planted):
-    """The full workload: every info value, and the factor of a sample of items."""
+    """The full workload: every info value and every item's factor against the
+    oracle (run on all host threads), compared 64 items at a time."""
     import torch
     import dense_linear_algebra_potrf_amd as bl
     n, batch = 512, 1024
@@ -100,27 +101,148 @@ def test_config_fp64_n512_b1024(planted):
             k = int(rng.choice([0, 5, 224, 250, 480, 511]))
             a[b, k, k] = -a[b, k, k]
             want[b] = k + 1
-    t = torch.from_numpy(syn.to_colmajor(a)).cuda()
+    buf = syn.to_colmajor(a)
+    t = torch.from_numpy(buf).cuda()
     info = bl.potrf(t, "L", n=n, batch=batch)
     torch.cuda.synchronize()
     info = info.cpu().numpy()
     assert np.array_equal(info, want)
     out = t.cpu().numpy().reshape(batch, n * n)
     del t
-    sample = np.array(sorted(set([0, 1, 63, 64, 65, 511, 512, 1023] +
-                                 list(np.random.default_rng(5).integers(0, batch, 8)))))
-    sub = a[sample]
-    ref = syn.to_colmajor(sub)
-    info_ref = oracle.potrf(ref, "L", n, len(sample))
-    assert np.array_equal(info_ref, want[sample])
-    got = syn.from_colmajor(out[sample].ravel(), n, n, len(sample))
-    exp = syn.from_colmajor(ref, n, n, len(sample))
-    ok = np.nonzero(info_ref == 0)[0]
-    if ok.size:
-        err = rel_err_triangle(got, exp, "L", ok)
-        assert err.max() <= TOL["f64"], f"factor error {err.max():.3e}"
-        assert factor_residual(sub, got, "L", ok).max() <= RESIDUAL_BOUND
-    # upper triangle untouched on every sampled item
+    info_ref = oracle.potrf(buf, "L", n, batch)          # in place: buf now holds the oracle's factor
+    assert np.array_equal(info_ref, want)
+    ref = buf.reshape(batch, n * n)
     iu = np.triu_indices(n, 1)
-    src = syn.from_colmajor(syn.to_colmajor(sub), n, n, len(sample))
-    assert np.array_equal(got[:, iu[0], iu[1]], src[:, iu[0], iu[1]])
+    worst_err, worst_res = 0.0, 0.0
+    for b0 in range(0, batch, 64):
+        idx = np.arange(b0, min(batch, b0 + 64))
+        got = syn.from_colmajor(out[idx].ravel(), n, n, len(idx))
+        exp = syn.from_colmajor(ref[idx].ravel(), n, n, len(idx))
+        ok = np.nonzero(info_ref[idx] == 0)[0]
+        if ok.size:
+            err = rel_err_triangle(got, exp, "L", ok)
+            res = factor_residual(a[idx], got, "L", ok)
+            worst_err, worst_res = max(worst_err, err.max()), max(worst_res, res.max())
+        # the upper triangle is untouched on every item
+        assert np.array_equal(got[:, iu[0], iu[1]], a[idx][:, iu[0], iu[1]])
+    record_error("potrf", "config fp64 n=512 b1024" + (" planted" if planted else ""), "f64",
+                 "L", n, batch, factor_rel=worst_err, residual=worst_res)
+    assert worst_err <= TOL["f64"], f"factor error {worst_err:.3e}"
+    assert worst_res <= RESIDUAL_BOUND
+
+
+# ---------------------------------------------------------------- ill-conditioned inputs
+def ill_conditioned(n: int, batch: int, dt: str, seed: int, delta: float) -> np.ndarray:
+    """A = G G^H / n + delta I (G square Gaussian), so kappa_2(A) is about 4 / delta."""
+    a = syn.spd_matrices(n, batch, "c128" if syn.is_complex(dt) else "f64", seed=seed)
+    a = a - (1.0 - delta) * np.eye(n)[None]
+    return a.astype(syn.np_dtype(dt))
+
+
+@pytest.mark.parametrize("n", [256, 512])
+@pytest.mark.parametrize("uplo", ["L", "U"])
+def test_blocked_fp64_ill_conditioned(n, uplo):
+    """kappa_2(A) ~ 1e3..1e4: the blocked family's triangular solves go through
+    explicit inverses of its diagonal blocks, whose error grows with their
+    condition number.  First-order perturbation theory bounds the relative
+    Frobenius error of a Cholesky factor computed in precision u by about
+    n u kappa_2(A), for the GPU result and the oracle alike, so the two differ
+    by at most 2 n u kappa_2(A) (per item, kappa from the eigenvalues)."""
+    batch = 8
+    a = ill_conditioned(n, batch, "f64", seed=n + 7, delta=1e-3)
+    ev = np.linalg.eigvalsh(a)
+    kappa = ev[:, -1] / ev[:, 0]
+    assert kappa.min() > 1e3
+    u = np.finfo(np.float64).eps / 2
+    buf = syn.to_colmajor(a)
+    ref = buf.copy()
+    info_ref = oracle.potrf(ref, uplo, n, batch)
+    out, info = gpu_potrf(buf, uplo, n, batch, n, n * n, family="blocked")
+    assert (info_ref == 0).all() and np.array_equal(info, info_ref)
+    got = syn.from_colmajor(out, n, n, batch)
+    exp = syn.from_colmajor(ref, n, n, batch)
+    err = rel_err_triangle(got, exp, uplo)
+    bound = 2 * n * u * kappa
+    record_error("potrf", f"ill-conditioned kappa<={kappa.max():.2e}", "f64", uplo, n, batch,
+                 factor_rel=err.max(), bound_min=bound.min())
+    assert (err <= bound).all(), f"error {err.max():.3e} against bound {bound.min():.3e}"
+    assert factor_residual(a, got, uplo).max() <= RESIDUAL_BOUND
+
+
+@pytest.mark.parametrize("dt", ["f32", "c64"])
+def test_blocked_fp32_ill_conditioned_against_exact(dt):
+    """Single precision at kappa_2 ~ 4e2: the factor computed in double from the
+    same rounded input is exact to single precision, so both the GPU result and
+    the oracle can be measured against it; the blocked family (explicit inverses
+    of its diagonal blocks) must stay within 4x the oracle's own error plus
+    n u."""
+    n, batch = 300, 8
+    a = ill_conditioned(n, batch, dt, seed=11, delta=1e-2)
+    wide = "c128" if dt == "c64" else "f64"
+    exact = syn.to_colmajor(a.astype(syn.np_dtype(wide)))
+    assert (oracle.potrf(exact, "L", n, batch) == 0).all()
+    ref = syn.to_colmajor(a)
+    assert (oracle.potrf(ref, "L", n, batch) == 0).all()
+    out, info = gpu_potrf(syn.to_colmajor(a), "L", n, batch, n, n * n, family="blocked")
+    assert (info == 0).all()
+    ex = syn.from_colmajor(exact, n, n, batch)
+    e_gpu = rel_err_triangle(syn.from_colmajor(out, n, n, batch), ex, "L")
+    e_orc = rel_err_triangle(syn.from_colmajor(ref, n, n, batch), ex, "L")
+    u = np.finfo(np.float32).eps / 2
+    record_error("potrf", "ill-conditioned vs exact", dt, "L", n, batch, gpu_vs_exact=e_gpu.max(),
+                 oracle_vs_exact=e_orc.max())
+    assert (e_gpu <= 4 * e_orc + n * u).all()
+
+
+# ---------------------------------------------------------------- info across panels
+@pytest.mark.parametrize("dt", ["f32", "f64", "c64", "c128"])
+@pytest.mark.parametrize("uplo", ["L", "U"])
+def test_blocked_info_first_failure_nan_and_stale_pivot(dt, uplo):
+    """The info cases of the tiny and LDS families at an order whose plants fall
+    in different 64-column panels: two plants (the first wins), a NaN pivot, a
+    zero pivot behind a negative one, the last column, and the stale-pivot trap
+    straddling a panel boundary (only its Schur pivot fails)."""
+    n = 200
+    a = syn.spd_matrices(n, 6, dt, seed=19)
+    a[0, 3, 3] *= -1
+    a[0, 150, 150] *= -1                     # two plants in different panels: the first wins
+    a[1, 0, 0] = syn.nan_value(dt)           # NaN pivot
+    a[2, 199, 199] = 0
+    a[2, 70, 70] *= -1
+    a[3, n - 1, n - 1] = -a[3, n - 1, n - 1]
+    stale = np.eye(n)
+    stale[63:66, 63:66] = [[1, .75, .75], [.75, 1, -.75], [.75, -.75, 1]]
+    a[4] = stale.astype(a.dtype)             # columns 63 | 64 65: the Schur pivot of column 66 fails
+    _, _, info = check_potrf(a, uplo, family="blocked", label="blocked-info")
+    assert list(info) == [4, 1, 71, n, 66, 0]
+
+
+# ---------------------------------------------------------------- saturating batches on the device
+def _device_replicas(one: np.ndarray, batch: int):
+    """A device batch of `batch` copies of one column-major matrix."""
+    import torch
+    src = torch.from_numpy(syn.to_colmajor(one)).cuda()
+    return src.repeat(batch)
+
+
+def _bits(t):
+    import torch
+    return t.view(torch.int64) if t.element_size() >= 8 or t.is_complex() else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("dt,uplo,n", [("f64", "L", 300), ("c64", "U", 200)])
+def test_blocked_saturating_batch_is_uniform(dt, uplo, n):
+    """16384 identical items (every compute unit busy, several workgroups each)
+    give the solo result bit for bit; compared on the device."""
+    import torch
+    import dense_linear_algebra_potrf_amd as bl
+    one = syn.spd_matrices(n, 1, dt, seed=8)
+    solo = _device_replicas(one, 1)
+    bl.potrf(solo, uplo, n=n, batch=1, family="blocked")
+    batch = 16384
+    announce("blocked saturating", dt, uplo, n, batch)
+    many = _device_replicas(one, batch)
+    info = bl.potrf(many, uplo, n=n, batch=batch, family="blocked")
+    torch.cuda.synchronize()
+    assert int((info != 0).sum()) == 0
+    assert torch.equal(_bits(many).view(batch, -1), _bits(solo).view(1, -1).expand(batch, -1))

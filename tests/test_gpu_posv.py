@@ -1,8 +1,7 @@
 """GPU parity of the fused posv (factor + forward + backward solve) against the
-CPU oracle, through the C ABI.  info bit-exact; factor within the element
-type's tolerance; X within 10x that tolerance per item (the solve amplifies the
-factor's rounding by about the condition number, <= 5 here) and residual
-||B - A X|| <= 10 n eps ||A|| ||X||; B unchanged for failed items."""
+CPU oracle, through the C ABI.  info bit-exact; factor and X both within the
+element type's tolerance (1e-4 fp32/cfloat, 1e-11 fp64/cdouble) per item, and
+residual ||B - A X|| <= 10 n eps ||A|| ||X||; B unchanged for failed items."""
 from __future__ import annotations
 
 import numpy as np

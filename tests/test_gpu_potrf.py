@@ -92,15 +92,22 @@ def test_lds_poison_and_padding(dt, uplo):
 
 @pytest.mark.parametrize("dt", ["f32", "c64"])
 def test_lds_packed_batch_is_independent(dt):
+    """16384 identical items plus a ragged tail (several workgroups resident per
+    compute unit) give the solo result bit for bit; compared on the device."""
+    import torch
+    import dense_linear_algebra_potrf_amd as bl
     n = 50
-    one = syn.spd_matrices(n, 1, dt, seed=5)
-    solo_out, _ = gpu_potrf(syn.to_colmajor(one), "U", n, 1, n, n * n, family="lds")
-    batch = 3001
-    out, info = gpu_potrf(syn.to_colmajor(np.repeat(one, batch, axis=0)), "U", n, batch, n,
-                          n * n, family="lds")
-    assert (info == 0).all()
-    res = out.reshape(batch, n * n)
-    assert bits_equal(res, np.broadcast_to(solo_out.reshape(1, n * n), res.shape))
+    one = torch.from_numpy(syn.to_colmajor(syn.spd_matrices(n, 1, dt, seed=5))).cuda()
+    solo = one.clone()
+    bl.potrf(solo, "U", n=n, batch=1, family="lds")
+    batch = 16384 + 3
+    announce("lds saturating", dt, n, batch)
+    many = one.repeat(batch)
+    info = bl.potrf(many, "U", n=n, batch=batch, family="lds")
+    torch.cuda.synchronize()
+    assert int((info != 0).sum()) == 0
+    iv = torch.int64 if many.element_size() >= 8 else torch.int32
+    assert torch.equal(many.view(iv).view(batch, -1), solo.view(iv).view(1, -1).expand(batch, -1))
 
 
 @pytest.mark.parametrize("planted", [False, True])
