@@ -34,6 +34,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+from dense_linear_algebra_potrf_amd import metrics  # noqa: E402  (host-side byte and flop models)
+
 METRIC = "batched potrf matrices/s + GB/s (% HBM peak) fp32 n=33; GFLOP/s fp64 n=512"
 
 CONFIGS = {
@@ -225,16 +227,37 @@ def attach_traffic(name: str, res: dict) -> None:
     res["roofline"]["traffic"] = rec.get("traffic_bytes")
 
 
-def cpu_baseline(name: str, cpu_seconds: float = 16.0) -> dict:
-    """The oracle on the host cores, on a bounded sample of the same workload
-    (about cpu_seconds of CPU work: wall time times threads)."""
-    import numpy as np
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def host_threads() -> int:
+    """Host threads the oracle may use: the process's CPU share, at most 16 (the
+    host CPU share of one GPU on the benchmark machines)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _oracle_rate(name: str, threads: int, cpu_seconds: float) -> tuple[float, int, int, float]:
+    """(matrices/s, matrices done, matrices per pass, wall s) of the oracle on a
+    sample of the workload, run for about cpu_seconds of CPU time (wall x threads)."""
     import oracle
     cfg = CONFIGS[name]
-    threads = max(1, min(16, os.cpu_count() or 1))
+    n = cfg["n"]
     budget_s = cpu_seconds / threads
-    n, dt = cfg["n"], cfg["dt"]
-    per = max(1, min(cfg["batch"], int(2e8 // max(1, n ** 3))))   # first sample size
+    # one pass is about 0.2 s of single-thread work at ~1 GFLOP/s, a multiple of the threads
+    per = max(threads, min(cfg["batch"], int(2e8 // max(1, n ** 3)) * threads))
     sample = dict(cfg, batch=per)
     abuf, bbuf = make_input(sample)
     done, t = 0, 0.0
@@ -248,9 +271,25 @@ def cpu_baseline(name: str, cpu_seconds: float = 16.0) -> dict:
             oracle.posv(a, b, cfg["uplo"], n, cfg["nrhs"], per, nthreads=threads)
         t += time.perf_counter() - t0
         done += per
-    return {"value": done / t, "unit": "matrices/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} matrices ({per} per pass) of: {describe(cfg)}; "
-                      f"{t:.2f} s wall on {threads} threads"}
+    return done / t, done, per, t
+
+
+def cpu_baseline(name: str, cpu_seconds: float = 16.0) -> dict:
+    """The oracle (as it stands: unblocked column Cholesky, no FMA contraction)
+    on the host, on a bounded sample of the same workload: about cpu_seconds of
+    CPU time on all host threads, and a quarter of that on one thread."""
+    cfg = CONFIGS[name]
+    threads = host_threads()
+    rate, done, per, wall = _oracle_rate(name, threads, cpu_seconds)
+    rate1, done1, _, wall1 = _oracle_rate(name, 1, cpu_seconds / 4)
+    flops = metrics.potrf_flops(cfg["n"], cfg["dt"]) if cfg["op"] == "potrf" else \
+        metrics.posv_flops(cfg["n"], cfg["nrhs"], cfg["dt"])
+    return {"value": rate, "unit": "matrices/s", "cores": threads, "kind": "oracle",
+            "gflops": rate * flops / 1e9,
+            "value_1thread": rate1, "gflops_1thread": rate1 * flops / 1e9,
+            "cpu_model": cpu_model(),
+            "sample": f"{done} matrices ({per} per pass) of: {describe(cfg)}; {wall:.2f} s wall "
+                      f"on {threads} threads; one thread: {done1} matrices in {wall1:.2f} s"}
 
 
 def copy_mode(mib: int, reps: int) -> None:
@@ -334,6 +373,8 @@ def main(argv=None) -> int:
             r = bench_config(name, max(3, min(a.steps, 10)), max(1, min(a.warmup, 3)),
                              use_graph=not a.no_graph)
             attach_traffic(name, r)
+            if not a.no_cpu:
+                r["cpu_baseline"] = cpu_baseline(name, cpu_seconds=6.0)
             sec[name] = r
             print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step, {r['gbs']:.0f} GB/s, "
                   f"{r['gflops']:.0f} GFLOP/s", file=sys.stderr, flush=True)

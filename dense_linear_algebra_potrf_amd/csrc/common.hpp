@@ -143,6 +143,23 @@ __device__ __forceinline__ void pivot_sqrt_rsq(double d, double& sq, double& rsq
 __device__ __forceinline__ double pivot_sqrt(double d) { double s, r; pivot_sqrt_rsq(d, s, r); return s; }
 __device__ __forceinline__ double pivot_rsq(double d) { double s, r; pivot_sqrt_rsq(d, s, r); return r; }
 
+// All three terms of a pivot, 1/d, 1/sqrt(d) and sqrt(d), from one reciprocal
+// square root rs: 1/d = rs rs and sqrt(d) = d rs.  The hardware reciprocal,
+// square root and reciprocal square root each issue at a quarter of the
+// vector rate, so one of them in place of three shortens every column step.
+// float: rs within about 1 ulp, so each term is within a few ulp.  double:
+// rs and sqrt(d) from the refined pair above.  A pivot that is not > 0 gives
+// NaN or infinity in some term, as it should: that matrix has already failed.
+__device__ __forceinline__ void pivot_terms(float d, float& inv, float& rs, float& sq) {
+    rs = __builtin_amdgcn_rsqf(d);
+    inv = rs * rs;
+    sq = d * rs;
+}
+__device__ __forceinline__ void pivot_terms(double d, double& inv, double& rs, double& sq) {
+    pivot_sqrt_rsq(d, sq, rs);
+    inv = rs * rs;
+}
+
 // ---------------------------------------------------------------- compile-time loops
 template <int V> using ic = std::integral_constant<int, V>;
 
@@ -204,7 +221,6 @@ constexpr int kBufFlags = 0x00020000;   // gfx9-family descriptor word 3 (raw, d
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, kBufFlags);
 }
-
 // soff is a wave-uniform byte offset (a scalar register) added to off; only off
 // takes part in the range check, so a masked off stays out of range.
 template <typename T>

@@ -181,7 +181,24 @@ __device__ __forceinline__ T lane_read(const T& x, int src) {
 // 0; a step reads them from LDS where it uses them (broadcast reads), so no
 // copy of the column is held in registers.  Rows above j write to a spare
 // slot at NB.
-template <typename T, int P, int R, bool UPPER, int NRHS, int ROWW>
+// The pivot terms of a step: from one reciprocal square root (pivot_terms)
+// where ONE_RSQ, else from three separate quarter-rate instructions.  Which is
+// faster depends on the window: the single one shortens the step, but the
+// compiler then schedules the window with more registers, and for the n = 33
+// window (11 x 3) that costs a wavefront per SIMD (measured 43.4 against 42.6
+// us at b16384), while the n = 17 window gains (24.4 against 25.8 us).
+template <bool ONE_RSQ, typename Rt>
+__device__ __forceinline__ void step_pivot(Rt d, Rt& inv, Rt& rs, Rt& sq) {
+    if constexpr (ONE_RSQ) {
+        pivot_terms(d, inv, rs, sq);
+    } else {
+        inv = pivot_rcp(d);
+        rs = pivot_rsq(d);
+        sq = pivot_sqrt(d);
+    }
+}
+
+template <typename T, int P, int R, bool UPPER, int NRHS, int ROWW, bool ONE_RSQ>
 __device__ __forceinline__ void factor_rows(T (&a)[R][P * R], typename Traits<T>::R (&invd)[R],
                                             uint32_t* xbuf, int p, int q, int32_t& inf)
 {
@@ -213,8 +230,8 @@ __device__ __forceinline__ void factor_rows(T (&a)[R][P * R], typename Traits<T>
         constexpr int rj = j / P;
         const Rt d = re(colv(j, j));
         inf = (inf == 0 && !(d > Rt(0))) ? (j + 1) : inf;
-        const Rt inv = pivot_rcp(d);
-        const Rt rs = pivot_rsq(d);
+        Rt inv, rs, sq;
+        step_pivot<ONE_RSQ>(d, inv, rs, sq);
         T t[R];
         static_for<rj, R>([&](auto rr) {
             constexpr int r = rr;
@@ -240,7 +257,7 @@ __device__ __forceinline__ void factor_rows(T (&a)[R][P * R], typename Traits<T>
             if constexpr (r == rj) {
                 // the one row block that holds row j itself
                 const bool diag = (q + r * P) == j;
-                a[r][j] = select(diag, diag_value<T>(pivot_sqrt(d), UPPER), scale(a[r][j], rs));
+                a[r][j] = select(diag, diag_value<T>(sq, UPPER), scale(a[r][j], rs));
                 if constexpr (NRHS > 0) invd[r] = diag ? rs : invd[r];
             } else {
                 a[r][j] = scale(a[r][j], rs);
@@ -261,7 +278,7 @@ __device__ __forceinline__ void factor_rows(T (&a)[R][P * R], typename Traits<T>
 // read just before its use and then waits for it, one LDS round trip per
 // read.  The exchange buffer layout and the scratch slots are those of
 // factor_rows.
-template <typename T, bool UPPER, int NRHS, int ROWW>
+template <typename T, bool UPPER, int NRHS, int ROWW, bool ONE_RSQ>
 __device__ __forceinline__ void factor_rows_lane(T (&a)[1][64], typename Traits<T>::R (&invd)[1],
                                                  uint32_t* xbuf, int q, int32_t& inf)
 {
@@ -279,8 +296,8 @@ __device__ __forceinline__ void factor_rows_lane(T (&a)[1][64], typename Traits<
     publish(ic<0>{});
     wave_lds_sync();
     Rt d = re(lane_read(a[0][0], 0));
-    Rt inv = pivot_rcp(d);
-    Rt rs = pivot_rsq(d);
+    Rt inv, rs, sq;
+    step_pivot<ONE_RSQ>(d, inv, rs, sq);
     T t = scale(a[0][0], inv);
     static_for<0, NB>([&](auto jj) {
         constexpr int j = jj;
@@ -306,7 +323,7 @@ __device__ __forceinline__ void factor_rows_lane(T (&a)[1][64], typename Traits<
         };
         if constexpr (BULK) fetch(ic<0>{});
         inf = (inf == 0 && !(d > Rt(0))) ? (j + 1) : inf;
-        Rt d_n = d, inv_n = inv, rs_n = rs;
+        Rt d_n = d, inv_n = inv, rs_n = rs, sq_n = sq;
         T t_n = t;
         if constexpr (j + 1 < NB) {
             // column j + 1 first: it feeds the next pivot and the next exchange
@@ -314,12 +331,11 @@ __device__ __forceinline__ void factor_rows_lane(T (&a)[1][64], typename Traits<
             publish(ic<j + 1>{});
             wave_lds_sync();
             d_n = re(lane_read(a[0][j + 1], j + 1));
-            inv_n = pivot_rcp(d_n);
-            rs_n = pivot_rsq(d_n);
+            step_pivot<ONE_RSQ>(d_n, inv_n, rs_n, sq_n);
             t_n = scale(a[0][j + 1], inv_n);
         }
         const bool diag = q == j;
-        a[0][j] = select(diag, diag_value<T>(pivot_sqrt(d), UPPER), scale(a[0][j], rs));
+        a[0][j] = select(diag, diag_value<T>(sq, UPPER), scale(a[0][j], rs));
         if constexpr (NRHS > 0) invd[0] = diag ? rs : invd[0];
         if constexpr (BULK) {
             static_for<0, NC>([&](auto cc) {
@@ -333,6 +349,7 @@ __device__ __forceinline__ void factor_rows_lane(T (&a)[1][64], typename Traits<
         d = d_n;
         inv = inv_n;
         rs = rs_n;
+        sq = sq_n;
         t = t_n;
     });
 }
@@ -374,6 +391,17 @@ template <typename T> constexpr int slab_tile_words() { return 64 * slab_pitch_w
 // orders up to 18); beyond that the image limits the wavefronts per CU.
 constexpr int kPackedLowerMaxOrder = 12;
 constexpr int kPackedUpperMaxBytes = 12 * 1024;
+
+// Windows whose steps take their pivot terms from one reciprocal square root
+// (measured on MI355X; the others keep three separate instructions): the
+// n = 17 window (17 x 1), the one-matrix-per-wavefront windows (64 x 1) and
+// the fused posv window of orders 25..32 (16 x 2).
+template <typename T, int P, int R, int NRHS>
+constexpr bool one_rsq_window() {
+    constexpr bool f32 = std::is_same<T, float>::value;
+    return (f32 && P == 17 && R == 1) || (P == 64 && R == 1) ||
+           (f32 && NRHS > 0 && P == 16 && R == 2);
+}
 
 // NRHS = 0: potrf.  NRHS > 0: posv for up to NRHS right-hand sides (nrhs at
 // run time), with the factor kept in registers for both triangular solves.
@@ -565,10 +593,11 @@ __global__ __launch_bounds__(PACKED ? 64 : 64 * kTinyWaves) void potrf_tiny_kern
 
     int32_t inf = 0;
     Rt invd[R];                 // 1 / L(i, i) of each held row (used by the solves)
+    constexpr bool ONE_RSQ = one_rsq_window<T, P, R, NRHS>();
     if constexpr (P == 64 && R == 1)
-        factor_rows_lane<T, UPPER, NRHS, ROWW>(a, invd, xbuf, q, inf);
+        factor_rows_lane<T, UPPER, NRHS, ROWW, ONE_RSQ>(a, invd, xbuf, q, inf);
     else
-        factor_rows<T, P, R, UPPER, NRHS, ROWW>(a, invd, xbuf, p, q, inf);
+        factor_rows<T, P, R, UPPER, NRHS, ROWW, ONE_RSQ>(a, invd, xbuf, p, q, inf);
 
     if constexpr (NRHS > 0)
         tiny_solves<T, P, R, NRHS>(a, invd, xbuf, PARTS * ROWW, ROWW, p, q, live, n,
