@@ -46,10 +46,15 @@ CONFIGS = {
     "posv_f32_L_n32_r4_b16384": dict(op="posv", dt="f32", uplo="L", n=32, nrhs=4, batch=16384, seed=1003),
     "potrf_c64_U_n64_b16384": dict(op="potrf", dt="c64", uplo="U", n=64, batch=16384, seed=1004),
     "potrf_f64_L_n512_b1024": dict(op="potrf", dt="f64", uplo="L", n=512, batch=1024, seed=1005),
+    # beyond the listed workloads: a mid order (the blocked family at n = 128) and
+    # the complex blocked path at the largest order
+    "potrf_f32_L_n128_b8192": dict(op="potrf", dt="f32", uplo="L", n=128, batch=8192, seed=1006),
+    "potrf_c64_L_n512_b1024": dict(op="potrf", dt="c64", uplo="L", n=512, batch=1024, seed=1007),
 }
 PRIMARY = "potrf_f32_L_n33_b16384"
 SECONDARY = ["potrf_f32_L_n17_b32768", "potrf_f32_L_n8_b1024", "potrf_f32_L_n8_b1048576",
-             "posv_f32_L_n32_r4_b16384", "potrf_c64_U_n64_b16384", "potrf_f64_L_n512_b1024"]
+             "posv_f32_L_n32_r4_b16384", "potrf_c64_U_n64_b16384", "potrf_f64_L_n512_b1024",
+             "potrf_f32_L_n128_b8192", "potrf_c64_L_n512_b1024"]
 
 
 def describe(cfg: dict) -> str:
@@ -200,8 +205,12 @@ def bench_config(name: str, steps: int, warmup: int, use_graph: bool = True) -> 
         "alg_bytes_per_call": byts,
         "alg_flops_per_call": flops,
     }
-    # roofline of the dominant kernel (one launch per call for the single-launch families)
-    bound = "mfma" if (dt in ("f64", "c128") and n >= 256) else "hbm"
+    # roofline of the dominant kernel (one launch per call for the single-launch
+    # families): the matrix-core peak of the element type where the algorithmic
+    # flops per algorithmic byte exceed that peak's ridge against 8 TB/s, HBM
+    # otherwise
+    ridge = peak_tf * 1e12 / (metrics.HBM_PEAK_GBS * 1e9)
+    bound = "mfma" if flops / byts > ridge else "hbm"
     if bound == "hbm":
         ach = byts / (ms_kernel * 1e-3) / 1e9
         res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": metrics.HBM_PEAK_GBS,

@@ -102,8 +102,8 @@ const char* dtype_name(DT dt) {
 
 // ---------------------------------------------------------------- dispatcher thresholds
 // Largest order the dispatcher sends to the tiny family, per element type;
-// the LDS family takes over above it up to its capacity, the blocked family
-// beyond.  Values come from measurements of both families on MI355X.
+// above it the LDS family up to auto_lds_cut, the blocked family beyond.
+// Values come from measurements of the families on MI355X.
 int auto_tiny_cut(DT dt) {
     switch (dt) {
     case DT::F32: return 64;    // the 64 x 1 window: 184 us against 392 at n=48 (b16384)
@@ -153,10 +153,29 @@ bool family_can_run_potrf(int fam, DT dt, int n, int64_t lda, int64_t stride) {
     return false;
 }
 
+// Largest order the dispatcher sends to the LDS family (above the tiny cut);
+// the blocked family takes everything above it.  From a sweep of the three
+// families on MI355X at orders 48..256 (batches of 16384 or 512 MB, both uplo,
+// us per call, LDS against blocked): the real types lose on the LDS family at
+// every order it serves above 64 (fp32 n=65 2441 against 1340, n=96 3094
+// against 1217; fp64 n=65 2716 against 1404, n=96 1814 against 662), the
+// complex types win on it (cfloat n=65 2897 against 5444, n=96 1934 against
+// 2572; cdouble n=48 1272 against 3470, n=64 1690 against 1976).
+int auto_lds_cut(DT dt) {
+    switch (dt) {
+    case DT::F32: return 0;
+    case DT::F64: return 0;
+    case DT::C64: return 96;
+    case DT::C128: return 64;
+    }
+    return 0;
+}
+
 int auto_potrf_family(DT dt, int n, int64_t lda, int64_t stride) {
     const bool tiny = family_can_run_potrf(bl::FAM_TINY, dt, n, lda, stride);
     if (tiny && n <= auto_tiny_cut(dt)) return bl::FAM_TINY;
-    if (family_can_run_potrf(bl::FAM_LDS, dt, n, lda, stride)) return bl::FAM_LDS;
+    if (n <= auto_lds_cut(dt) && family_can_run_potrf(bl::FAM_LDS, dt, n, lda, stride))
+        return bl::FAM_LDS;
     if (family_can_run_potrf(bl::FAM_BLOCKED, dt, n, lda, stride)) return bl::FAM_BLOCKED;
     if (tiny) return bl::FAM_TINY;
     return bl::FAM_AUTO;

@@ -38,6 +38,11 @@ namespace tiny_detail {
 // window ran 15% slower with four per workgroup).
 constexpr int kTinyWaves = 1;
 
+// At most this many workgroups per launch: a dispatch counts its work-items in
+// 32 bits, and a batch of 2^30 matrices of order <= 4 would need 2^26 one-wave
+// workgroups.  Larger batches run as several launches over consecutive slices.
+constexpr int64_t kTinyMaxGrid = int64_t(1) << 24;
+
 // Dwords per partition row of the column buffer: >= nb * D, of the form
 // 32 m + 4, so partitions of a wave start on different 16-byte bank groups.
 constexpr int tiny_row_words(int nb, int d) {
@@ -782,6 +787,7 @@ bool geometry_t(bool upper, int n, int64_t lda, int64_t stride, int64_t batch, G
         g.threads = 64 * waves;
         g.panel = 0;
         g.grid = (batch + gw * waves - 1) / (gw * waves);
+        if (g.grid > kTinyMaxGrid) g.grid = kTinyMaxGrid;     // first launch of a sliced batch
         const int64_t sw = (upper && C::P == 64 && C::R == 1 && !packed) ? slab_tile_words<T>() : 0;
         g.lds = packed ? 4 * (xw > iw ? xw : iw) : int64_t(waves) * (xw > sw ? xw : sw) * 4;
     });
@@ -793,17 +799,28 @@ template <typename T, typename C, bool UPPER, int NRHS>
 hipError_t launch_tiny(int n, T* a, int64_t lda, int64_t stride, int64_t batch, int32_t* info,
                        T* b, int nrhs, int64_t ldb, int64_t strideB, hipStream_t s) {
     constexpr int G = 64 / C::P;
-    if constexpr (packed_wanted<T, C, UPPER>()) {
-        if (packed_layout<C>(n, lda, stride)) {
-            const int64_t grid = (batch + G - 1) / G;
-            return launch(potrf_tiny_kernel<T, C::P, C::R, UPPER, NRHS, true>, dim3((unsigned)grid),
-                          dim3(64), 0, s, a, n, lda, stride, batch, info, b, nrhs, ldb, strideB, G);
+    bool packed = false;
+    if constexpr (packed_wanted<T, C, UPPER>()) packed = packed_layout<C>(n, lda, stride);
+    const int gu = packed ? G : C::GU;                   // matrices per workgroup (one wavefront)
+    const int64_t per_launch = kTinyMaxGrid * gu;        // matrices per launch
+    hipError_t err = hipSuccess;
+    for (int64_t b0 = 0; b0 < batch && err == hipSuccess; b0 += per_launch) {
+        const int64_t nb = batch - b0 < per_launch ? batch - b0 : per_launch;
+        const dim3 grid((unsigned)((nb + gu - 1) / gu));
+        T* const as = a + b0 * stride;
+        int32_t* const is = info ? info + b0 : nullptr;
+        T* const bs = b ? b + b0 * strideB : nullptr;
+        if (packed) {
+            if constexpr (packed_wanted<T, C, UPPER>())
+                err = launch(potrf_tiny_kernel<T, C::P, C::R, UPPER, NRHS, true>, grid, dim3(64), 0, s,
+                             as, n, lda, stride, nb, is, bs, nrhs, ldb, strideB, gu);
+        } else {
+            err = launch(potrf_tiny_kernel<T, C::P, C::R, UPPER, NRHS, false>, grid,
+                         dim3(64 * kTinyWaves), 0, s, as, n, lda, stride, nb, is, bs, nrhs, ldb,
+                         strideB, gu);
         }
     }
-    constexpr int gu = C::GU;
-    const int64_t grid = (batch + gu * kTinyWaves - 1) / (gu * kTinyWaves);
-    return launch(potrf_tiny_kernel<T, C::P, C::R, UPPER, NRHS, false>, dim3((unsigned)grid),
-                  dim3(64 * kTinyWaves), 0, s, a, n, lda, stride, batch, info, b, nrhs, ldb, strideB, gu);
+    return err;
 }
 
 template <typename T>

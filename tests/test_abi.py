@@ -117,10 +117,15 @@ def test_route_auto_picks_by_size(lib):
     assert bl.route("f32", "L", 8, 1024)["family"] == "tiny"
     assert bl.route("f32", "L", 17, 32768)["family"] == "tiny"
     assert bl.route("c128", "U", 16, 64)["family"] == "tiny"
-    # the one-matrix-per-wavefront windows end each type's tiny range
+    # the one-matrix-per-wavefront windows end each type's tiny range; above it
+    # the real types go to the blocked family, the complex ones to the LDS family
+    # up to its measured cut
     for dt, top in (("f32", 64), ("f64", 64), ("c64", 64), ("c128", 32)):
         assert bl.route(dt, "L", top, 16384)["family"] == "tiny"
-        assert bl.route(dt, "U", top + 1, 16384)["family"] == "lds"
+    for dt, n, fam in (("f32", 65, "blocked"), ("f64", 96, "blocked"), ("c64", 65, "lds"),
+                       ("c64", 96, "lds"), ("c64", 97, "blocked"), ("c128", 33, "lds"),
+                       ("c128", 64, "lds"), ("c128", 65, "blocked")):
+        assert bl.route(dt, "U", n, 16384)["family"] == fam, (dt, n)
     # above the LDS family's capacity the complex types go to the blocked family
     assert bl.route("c64", "U", 128, 64)["family"] == "blocked"
     assert bl.route("c64", "L", 512, 64)["family"] == "blocked"
@@ -201,3 +206,14 @@ def test_counter_digest_follows_the_family_sources(tmp_path, monkeypatch):
     assert tiny1 != tiny0
     (csrc / "common.hpp").write_text("changed")
     assert bench.source_digest("tiny") != tiny1
+
+
+def test_tiny_grid_is_capped_for_huge_batches(lib):
+    """A batch of 2^30 matrices of order 4 (16 per wavefront) would need 2^26
+    one-wavefront workgroups; the tiny family launches it in slices of at most
+    2^24 workgroups, and the route reports the first slice's grid."""
+    r = bl.route("f32", "L", 4, 1 << 30, family="tiny")
+    assert r["grid"] == 1 << 24
+    assert r["grid"] * r["matrices_per_wave"] * (r["block_threads"] // 64) < (1 << 30)
+    small = bl.route("f32", "L", 4, 1000, family="tiny")
+    assert small["grid"] * small["matrices_per_wave"] >= 1000

@@ -87,3 +87,24 @@ def test_posv_tiny_beyond_2_31_elements():
     assert torch.equal(_bits(mb).view(batch, -1), _bits(sb).view(1, -1).expand(batch, -1))
     del ma, mb, info
     torch.cuda.empty_cache()
+
+
+def test_tiny_batch_sliced_over_several_launches():
+    """Order 2 packs 16 matrices per wavefront; 2^28 + 5 matrices need more than
+    2^24 workgroups, so the batch runs as two launches over consecutive slices.
+    Every item, on both sides of the slice boundary, must equal the solo result."""
+    import torch
+    import dense_linear_algebra_potrf_amd as bl
+    n, batch = 2, (1 << 28) + 5
+    assert bl.route("f32", "L", n, batch, family="tiny")["grid"] == 1 << 24
+    announce("sliced", f"n={n}", f"batch={batch}")
+    one = syn.to_colmajor(syn.spd_matrices(n, 1, "f32", seed=2))
+    solo = _replicas(one, 1)
+    bl.potrf(solo, "L", n=n, batch=1, family="tiny")
+    many = _replicas(one, batch)
+    info = bl.potrf(many, "L", n=n, batch=batch, family="tiny")
+    torch.cuda.synchronize()
+    assert int((info != 0).sum()) == 0
+    assert torch.equal(_bits(many).view(batch, -1), _bits(solo).view(1, -1).expand(batch, -1))
+    del many, info
+    torch.cuda.empty_cache()
