@@ -106,7 +106,11 @@ const char* dtype_name(DT dt) {
 // Values come from measurements of the families on MI355X.
 int auto_tiny_cut(DT dt) {
     switch (dt) {
-    case DT::F32: return 64;    // the 64 x 1 window: 184 us against 392 at n=48 (b16384)
+    // fp32: the 64 x 1 window (184 us against 392 at n=48, b16384), then the wide
+    // window of two wavefronts per matrix, 1.8-2.3x faster than the blocked family
+    // at every order 65..128 (n=65 589 us against 1339, n=97 802 against 1524,
+    // n=128 b8192 498 against 892; Upper alike)
+    case DT::F32: return 128;
     case DT::F64: return 64;    // 64 x 1: 324 us against 438 at n=33, 342 against 2593 at n=64
     case DT::C64: return 64;    // the 64 x 1 window beats the LDS family at 33..64
     case DT::C128: return 32;   // 32 x 1: 90-115 us against 321-993 at n=17..32

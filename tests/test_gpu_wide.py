@@ -1,0 +1,139 @@
+"""GPU parity of the tiny family's wide fp32 window (orders 65..128, one matrix
+per workgroup of two wavefronts, a row per lane) against the CPU oracle.
+
+Same bar as the other families: info bit-exact on every item, the referenced
+triangle within 1e-4 relative Frobenius error per item, the other triangle and
+the padding untouched.  The cases aim at what is particular to the window: the
+column exchange between the two wavefronts (failures and stale pivots on both
+sides of row 64), the two compile-time windows (96 and 128 columns, so orders
+96 / 97 and 128 are edges), rows beyond n inside a window, and batches beyond
+the launch's grid cap and beyond 2^31 elements.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import synthetic as syn
+from tests._gpu import announce, check_potrf
+
+pytestmark = pytest.mark.gpu
+
+UPLOS = ["L", "U"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    import dense_linear_algebra_potrf_amd as bl
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    bl.load_library()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _bits(t):
+    import torch
+    return t.view(torch.int32)
+
+
+def _replicas(one: np.ndarray, batch: int):
+    import torch
+    return torch.from_numpy(syn.to_colmajor(one)).cuda().repeat(batch)
+
+
+@pytest.mark.parametrize("uplo", UPLOS)
+def test_wide_every_order(uplo):
+    """Every order of the window, both triangles, with failures planted at
+    random columns in every seventh item."""
+    import dense_linear_algebra_potrf_amd as bl
+    for n in range(65, 129):
+        r = bl.route("f32", uplo, n, 41)
+        assert r["family"] == "tiny" and r["block_threads"] == 128, (n, r)
+        a = syn.spd_matrices(n, 41, "f32", seed=1000 + 2 * n + (uplo == "U"))
+        want = syn.plant_failures(a, seed=n, every=7)
+        check_potrf(a, uplo, family="tiny", expect_info=want, label="wide-every-order")
+
+
+@pytest.mark.parametrize("uplo", UPLOS)
+def test_wide_poison_and_padding(uplo):
+    """Padded layout (lda > n, stride > lda n) with NaN then sentinel fill in
+    the padding and the unreferenced triangle: nothing there is read or
+    written."""
+    for n in (65, 77, 96, 97, 120, 128):
+        a = syn.spd_matrices(n, 19, "f32", seed=n)
+        syn.plant_failures(a, seed=n, every=5)
+        for fill in (syn.nan_value("f32"), syn.sentinel("f32")):
+            check_potrf(a, uplo, family="tiny", padded=True, fill=fill, label="wide-poison")
+
+
+@pytest.mark.parametrize("uplo", UPLOS)
+@pytest.mark.parametrize("n", [90, 128])
+def test_wide_info_first_failure_nan_and_stale_pivot(uplo, n):
+    """The first failing column wins, on either wavefront's side of row 64; a
+    NaN pivot fails; a pivot that only goes non-positive in its Schur
+    complement fails at that column, here with the chain crossing from
+    wavefront 0's rows into wavefront 1's."""
+    a = syn.spd_matrices(n, 8, "f32", seed=31 + n)
+    a[0, 3, 3] *= -1
+    a[0, 70, 70] *= -1                        # two plants: the first wins
+    a[1, 0, 0] = syn.nan_value("f32")         # NaN pivot in the first column
+    a[2, 64, 64] = syn.nan_value("f32")       # first row of the second wavefront
+    a[3, n - 1, n - 1] = -a[3, n - 1, n - 1]  # last column
+    stale = np.eye(n)
+    idx = [63, 64, 65]
+    stale[np.ix_(idx, idx)] = [[1, .75, .75], [.75, 1, -.75], [.75, -.75, 1]]
+    a[4] = stale.astype(a.dtype)              # unit diagonal: only the Schur pivot of column 66 fails
+    a[5, 64, 64] = 0                          # exact zero pivot
+    a[6, 63, 63] *= -1                        # last row of the first wavefront
+    _, _, info = check_potrf(a, uplo, family="tiny", label="wide-info")
+    assert list(info) == [4, 1, 65, n, 66, 65, 64, 0]
+
+
+@pytest.mark.parametrize("uplo,n", [("L", 65), ("U", 128)])
+def test_wide_batch_beyond_the_grid_cap_is_uniform(uplo, n):
+    """More matrices than the launch's workgroups (2^20): every workgroup loops
+    over several matrices.  Identical items give the solo result bit for bit,
+    including the last ones; compared on the device."""
+    import torch
+    import dense_linear_algebra_potrf_amd as bl
+    batch = (1 << 20) + 5
+    r = bl.route("f32", uplo, n, batch)
+    assert r["family"] == "tiny" and r["grid"] == 1 << 20
+    one = syn.spd_matrices(n, 1, "f32", seed=2 * n)
+    solo = _replicas(one, 1)
+    bl.potrf(solo, uplo, n=n, batch=1)
+    announce("wide beyond grid cap", uplo, f"n={n}", f"batch={batch}")
+    many = _replicas(one, batch)
+    info = bl.potrf(many, uplo, n=n, batch=batch)
+    torch.cuda.synchronize()
+    assert int((info != 0).sum()) == 0
+    assert torch.equal(_bits(many).view(batch, -1), _bits(solo).view(1, -1).expand(batch, -1))
+    del many, info
+    torch.cuda.empty_cache()
+
+
+def test_wide_batch_of_distinct_items_matches_the_oracle_at_every_sampled_item():
+    """fp32 n=128 over 8192 distinct matrices (the secondary workload's
+    shape), Lower: every item against the oracle, in chunks."""
+    import torch
+    import dense_linear_algebra_potrf_amd as bl
+    import oracle
+    from tests._checks import TOL, rel_err_triangle
+    n, batch = 128, 8192
+    a = syn.spd_matrices(n, batch, "f32", seed=1006)
+    buf = syn.to_colmajor(a)
+    announce("wide distinct", f"n={n}", f"batch={batch}")
+    t = torch.from_numpy(buf).cuda()
+    info = bl.potrf(t, "L", n=n, batch=batch)
+    torch.cuda.synchronize()
+    assert int((info != 0).sum()) == 0
+    out = t.cpu().numpy()
+    worst = 0.0
+    for c0 in range(0, batch, 512):
+        ref = buf[c0 * n * n:(c0 + 512) * n * n].copy()
+        assert (oracle.potrf(ref, "L", n, 512, n, n * n) == 0).all()
+        got = syn.from_colmajor(out[c0 * n * n:(c0 + 512) * n * n], n, n, 512, n, n * n)
+        want = syn.from_colmajor(ref, n, n, 512, n, n * n)
+        worst = max(worst, float(rel_err_triangle(got, want, "L").max()))
+    assert worst <= TOL["f32"], worst
