@@ -107,10 +107,11 @@ const char* dtype_name(DT dt) {
 int auto_tiny_cut(DT dt) {
     switch (dt) {
     // fp32: the 64 x 1 window (184 us against 392 at n=48, b16384), then the wide
-    // window of two wavefronts per matrix, 1.8-2.3x faster than the blocked family
-    // at every order 65..128 (n=65 589 us against 1339, n=97 802 against 1524,
-    // n=128 b8192 498 against 892; Upper alike)
-    case DT::F32: return 128;
+    // window: 2.5-3.9x faster than the blocked family at 65..128 (two wavefronts,
+    // a row per lane: n=65 b16384 342 us against 1348, n=128 b8192 353 against
+    // 899), 1.4-1.5x at 129..192 (tiles: n=129 896 against 1245, n=192 b3640 498
+    // against 732); Upper alike
+    case DT::F32: return 192;
     case DT::F64: return 64;    // 64 x 1: 324 us against 438 at n=33, 342 against 2593 at n=64
     case DT::C64: return 64;    // the 64 x 1 window beats the LDS family at 33..64
     case DT::C128: return 32;   // 32 x 1: 90-115 us against 321-993 at n=17..32

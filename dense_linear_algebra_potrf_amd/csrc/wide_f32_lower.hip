@@ -1,5 +1,5 @@
 // Wide fp32 window of the tiny family, Lower (A = L L^H) (one translation unit
-// per triangle: each holds two large unrolled kernels).
+// per triangle: each holds large unrolled kernels).
 #include "wide_impl.hpp"
 
 namespace bl {

@@ -1,5 +1,5 @@
 // Wide fp32 window of the tiny family, Upper (A = U^H U) (one translation unit
-// per triangle: each holds two large unrolled kernels).
+// per triangle: each holds large unrolled kernels).
 #include "wide_impl.hpp"
 
 namespace bl {

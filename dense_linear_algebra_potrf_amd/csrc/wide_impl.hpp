@@ -1,26 +1,33 @@
-// Wide window of the tiny family (implementation header): orders 65..128 in
-// fp32, one workgroup of two wavefronts per matrix, each lane holding one row
-// of the matrix in registers.
+// Wide window of the tiny family (implementation header): fp32 orders 65..192,
+// one workgroup per matrix, the matrix held in the registers of several
+// wavefronts.
 //
 // Prior art: the BatchLAS perf_potrf page, section "potrf: the tiny tier"
 // (lane r owns row r and every value stays in registers) and section "The
 // LPanel tier" (one thread per row at mid orders).  Beyond 64 rows one
 // wavefront no longer holds a row per lane, and two rows per lane do not fit
-// the register file at a useful occupancy, so the rows are split over the
-// wavefronts of a workgroup: wavefront w holds rows 64 w .. 64 w + 63, lane l
-// row 64 w + l.  A row only has columns up to its diagonal, so wavefront w
-// keeps the columns below KE(w) = 64 (w + 1) (fixed at compile time for each
-// wavefront's code); wavefront 0 stops updating after column 63.
+// the register file at a useful occupancy, so the rows are spread over the
+// wavefronts of a workgroup.  Two layouts:
 //
-// The column recurrence is that of the tiny family (right-looking, the
-// Schur pivot never stale, the multiplier s_ij / d applied to the unscaled
-// column, failures as selects with the first failing column kept), with the
-// pivot column exchanged through LDS between the wavefronts: at step j every
-// lane has the entries of column j it needs in the buffer of parity j; it
-// updates its entry of column j + 1 first and publishes it to the other
-// buffer, then the rest of its row, and one workgroup barrier ends the step.
-// The barrier separates each column's stores from its reads, and the reads of
-// a buffer from its reuse two steps later.
+//   * rows (orders 65..128): two wavefronts, lane l of wavefront w holding row
+//     64 w + l whole.  A row only has columns up to its diagonal, so wavefront
+//     w keeps the columns below 64 (w + 1), fixed at compile time for each
+//     wavefront's code: wavefront 0 stops updating after column 63.
+//   * tiles (orders 129..192): the part of the matrix below the diagonal cut
+//     into tiles of 64 rows x 32 columns, one wavefront per tile (up to 12);
+//     lane l of the wavefront for row block rb and column block cb holds
+//     columns 32 cb .. 32 cb + 31 of row 64 rb + l.
+//
+// The column recurrence is that of the tiny family (right-looking, the Schur
+// pivot never stale, the multiplier s_ij / d applied to the unscaled column,
+// failures as selects with the first failing column kept).  Column j is
+// exchanged through an LDS buffer with one slot per row, double-buffered by
+// step parity; one workgroup barrier ends each step, which orders each column's
+// stores before its reads and the reads of a buffer before its reuse two steps
+// later.  The entries of column j a row's update needs lie in groups of 16
+// rows: lane q reads entry 16 g + (q mod 16) of group g, and each update takes
+// its row's value from the right lane of its row of 16 by a DPP broadcast
+// inside the multiply-add, so one LDS dword per lane feeds 16 updates.
 //
 // Loads and stores (Lower): lanes of a wavefront hold consecutive rows, so
 // each column is one coalesced access of 64 consecutive elements.  Upper reads
@@ -32,59 +39,97 @@
 namespace bl {
 namespace wide_detail {
 
-// Columns (and rows) served: NC = 96 or 128; two wavefronts per workgroup.
-template <int NC> struct WideShape {
-    static constexpr int NW = (NC + 63) / 64;
-    static constexpr int LD = 64 * NW + 4;   // floats per column buffer: a slot for every lane
-};
-
+constexpr int kWideRowsMaxOrder = 128;           // the rows layout serves 65..128
+constexpr int kWideMaxOrder = 192;               // the tiles layout 129..192
+constexpr int kTileCols = 32;                    // columns of a tile
+constexpr int kWideSlots = kWideMaxOrder + 4;    // slots of each column buffer
 constexpr int64_t kWideMaxGrid = int64_t(1) << 20;
 
-template <int NC, bool UPPER, bool ONE_RSQ>
-__global__ __launch_bounds__(64 * WideShape<NC>::NW) __attribute__((amdgpu_waves_per_eu(2))) void potrf_wide_kernel(
+// One matrix's buffer descriptor and the offsets of its elements.
+struct WideRow {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t lda_b;
+    // Column c's scalar offset, computed next to its use behind an opaque copy:
+    // otherwise all of them are computed once, hoisted out of the batch loop
+    // and held (spilled) for the whole factorisation.
+    template <bool UPPER>
+    __device__ __forceinline__ uint32_t col_off(int c) const {
+        uint32_t step = UPPER ? 4u : lda_b;
+        asm volatile("" : "+s"(step) : : "memory");
+        return uint32_t(c) * step;
+    }
+    // Row i's offset for its element of column c, or out of range for rows at
+    // or beyond n and for entries above the diagonal.
+    template <bool UPPER>
+    __device__ __forceinline__ uint32_t off(int i, int c, int n) const {
+        return (c <= i && i < n) ? (UPPER ? uint32_t(i) * lda_b : uint32_t(i) * 4u) : kBufOOB;
+    }
+};
+
+// The row index behind an opaque copy.  Everything derived from the row index
+// (masked offsets, the diagonal select) is formed from a fresh copy where it is
+// used: shared between the loads and the stores, or hoisted out of the batch
+// loop, those values would be held (and spilled) across the factorisation.
+__device__ __forceinline__ int opaque_row(int i) {
+    asm volatile("" : "+v"(i));
+    return i;
+}
+
+// Rank-1 update of a[K0..KE) with multiplier nt against the column entries
+// col[c0 + k], in groups of 16 rows with DPP row broadcasts.
+template <int K0, int KE, int N>
+__device__ __forceinline__ void wide_update(float (&a)[N], const float* col, int c0, int q16, float nt) {
+    if constexpr (K0 < KE) {
+        constexpr int G0 = K0 / 16, G1 = (KE + 15) / 16;
+        float cg[2];
+        cg[G0 & 1] = col[c0 + 16 * G0 + q16];
+        static_for<G0, G1>([&](auto gg) {
+            constexpr int g = gg;
+            if constexpr (g + 1 < G1) cg[(g + 1) & 1] = col[c0 + 16 * (g + 1) + q16];
+            constexpr int KB = cmax(K0, 16 * g);
+            static_for<KB, cmin(KE, 16 * g + 16)>([&](auto kk) {
+                constexpr int k = kk;
+                fma_bcast16<k - 16 * g, k == KB>(a[k], nt, cg[g & 1]);
+            });
+        });
+    }
+}
+
+// info: the first failing pivot (1-based), kept once set
+__device__ __forceinline__ void note_pivot(int32_t& inf, float d, int j) {
+    inf = (inf == 0 && !(d > 0.0f)) ? (j + 1) : inf;
+    // taken now: sunk into the final store, the select chain would keep every
+    // pivot alive across the factorisation
+    asm volatile("" : "+v"(inf));
+}
+
+// ---------------------------------------------------------------- rows layout
+// NC = 96 or 128 columns (two wavefronts; rows beyond 96 are idle for n <= 96).
+template <int NC, bool UPPER>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void potrf_wide_rows_kernel(
     float* __restrict__ A, int n, int64_t lda, int64_t stride, int64_t batch,
     int32_t* __restrict__ info)
 {
-    using Sh = WideShape<NC>;
-    constexpr int NW = Sh::NW, LD = Sh::LD;
-    __shared__ __attribute__((aligned(16))) float colbuf[2][LD];
-
+    __shared__ __attribute__((aligned(16))) float colbuf[2][kWideSlots];
     const int lane = threadIdx.x & 63;
+    const int q16 = lane & 15;                // lane within its row of 16 (DPP broadcasts)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int i0 = wave * 64 + lane;          // this lane's row
-    const uint32_t lda_b = uint32_t(lda) * 4u;
+    const int i = wave * 64 + lane;           // this lane's row
 
     // the whole matrix for the wavefront whose rows end at KE
     auto run = [&](auto kec, int64_t b) __attribute__((always_inline)) {
         constexpr int KE = decltype(kec)::value;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(A + b * stride);
-        // the row index hidden from the optimiser: the masked offsets are the
-        // same for every matrix, and hoisted out of the batch loop they would
-        // be held in registers across the factorisation
-        int i = i0;
-        asm volatile("" : "+v"(i));
-        const bool rowok = i < n;
-        const uint32_t rbase = rowok ? (UPPER ? uint32_t(i) * lda_b : uint32_t(i) * 4u) : kBufOOB;
-        // Column c's scalar offset is computed next to its use, behind an opaque
-        // copy: otherwise all of them are computed once, hoisted out of the batch
-        // loop and held (spilled) for the whole factorisation.
-        auto col_off = [&](int c) __attribute__((always_inline)) {
-            uint32_t step = UPPER ? 4u : lda_b;
-            asm volatile("" : "+s"(step) : : "memory");
-            return uint32_t(c) * step;
-        };
+        const WideRow m{make_rsrc(A + b * stride), uint32_t(lda) * 4u};
+        // Rows at or beyond n load as zero and are never stored; a row's update
+        // only reads the column entries of rows at or above it, so their values
+        // never reach a row below n.  Their first zero pivot (step n) only marks
+        // info n + 1, which is cleared at the end.
         float a[KE];
+        const int il = opaque_row(i);
         static_for<0, KE>([&](auto cc) {
             constexpr int c = cc;
-            // the diagonal block's upper part is never read (scratch slots)
-            uint32_t off = rbase;
-            if constexpr (c >= KE - 64) off = (c <= i) ? off : kBufOOB;
-            a[c] = buf_load<float>(rs, off, col_off(c));
+            a[c] = buf_load<float>(m.rs, m.off<UPPER>(il, c, n), m.col_off<UPPER>(c));
         });
-        // Rows at or beyond n load as zero and are never stored (rbase is out of
-        // range for them); a row's update only reads the column entries of rows
-        // at or above it, so their values never reach a row below n.  Their first
-        // zero pivot (step n) only marks info n + 1, which is cleared at the end.
         int32_t inf = 0;
         colbuf[0][i] = a[0];
         __syncthreads();
@@ -93,102 +138,160 @@ __global__ __launch_bounds__(64 * WideShape<NC>::NW) __attribute__((amdgpu_waves
             if constexpr (j < KE) {
                 const float* col = &colbuf[j & 1][0];
                 const float d = col[j];
-                inf = (inf == 0 && !(d > 0.0f)) ? (j + 1) : inf;
-                // taken now: sunk into the store at the end, the select chain
-                // would keep every pivot alive across the factorisation
-                asm volatile("" : "+v"(inf));
+                note_pivot(inf, d, j);
                 float inv, rsd, sq;
-                if constexpr (ONE_RSQ) {
-                    pivot_terms(d, inv, rsd, sq);
-                } else {
-                    inv = pivot_rcp(d);
-                    rsd = pivot_rsq(d);
-                    sq = pivot_sqrt(d);
-                }
+                pivot_terms(d, inv, rsd, sq);
                 const float t = a[j] * inv;
+                // the next column first, published for the next step
                 if constexpr (j + 1 < KE) {
                     a[j + 1] = fmadd(-t, col[j + 1], a[j + 1]);
                     colbuf[(j + 1) & 1][i] = a[j + 1];
                 }
-                // the rest of the row, 16 columns a batch with the next batch's
-                // reads issued ahead of this batch's updates
-                constexpr int K0 = j + 2, CH = 16;
-                if constexpr (K0 < KE) {
-                    constexpr int NCH = (KE - K0 + CH - 1) / CH;
-                    float cv[2][CH];
-                    auto fetch = [&](auto ch) {
-                        constexpr int c = ch;
-                        static_for<K0 + c * CH, cmin(KE, K0 + (c + 1) * CH)>([&](auto kk) {
-                            constexpr int k = kk;
-                            cv[c & 1][k - K0 - c * CH] = col[k];
-                        });
-                    };
-                    auto apply = [&](auto ch) {
-                        constexpr int c = ch;
-                        static_for<K0 + c * CH, cmin(KE, K0 + (c + 1) * CH)>([&](auto kk) {
-                            constexpr int k = kk;
-                            a[k] = fmadd(-t, cv[c & 1][k - K0 - c * CH], a[k]);
-                        });
-                    };
-                    fetch(ic<0>{});
-                    static_for<0, NCH>([&](auto ch) {
-                        constexpr int c = ch;
-                        __builtin_amdgcn_sched_barrier(0);
-                        if constexpr (c + 1 < NCH) fetch(ic<c + 1>{});
-                        apply(ch);
-                    });
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                wide_update<j + 2, KE>(a, col, 0, q16, -t);
                 // column j is final: to the matrix now (one coalesced column),
                 // which frees its register for the rest of the factorisation
-                const float lij = (i == j) ? sq : a[j] * rsd;
-                buf_store<float>(rs, (j <= i) ? rbase : kBufOOB, lij, col_off(j));
+                const int is = opaque_row(i);
+                const float lij = (is == j) ? sq : a[j] * rsd;
+                buf_store<float>(m.rs, m.off<UPPER>(is, j, n), lij, m.col_off<UPPER>(j));
             }
             __syncthreads();
         });
-        // the last wavefront reads every pivot (the others stop at their last row)
-        if (wave == NW - 1 && lane == 0 && info != nullptr) info[b] = inf > n ? 0 : inf;
+        // the second wavefront reads every pivot (the first stops at its last row)
+        if (wave == 1 && lane == 0 && info != nullptr) info[b] = inf > n ? 0 : inf;
     };
 
     for (int64_t b = blockIdx.x; b < batch; b += gridDim.x) {
-        if (NW == 1 || wave == 0) run(ic<64>{}, b);
+        if (wave == 0) run(ic<64>{}, b);
         else run(ic<NC>{}, b);
         __syncthreads();     // colbuf is reused by the next matrix
     }
 }
 
-// Orders served (fp32): above the one-wavefront windows, up to two wavefronts.
-constexpr int kWideMinOrder = 65, kWideMaxOrder = 128;
+// ---------------------------------------------------------------- tiles layout
+// Row block rb holds the column blocks that start below min(64 (rb + 1), n);
+// wavefronts are numbered row block by row block.
+__host__ __device__ constexpr int wide_col_blocks(int rb, int n) {
+    return ((64 * (rb + 1) < n ? 64 * (rb + 1) : n) + kTileCols - 1) / kTileCols;
+}
+__host__ __device__ constexpr int wide_tile_waves(int n) {
+    int w = 0;
+    for (int rb = 0; 64 * rb < n; ++rb) w += wide_col_blocks(rb, n);
+    return w;
+}
+static_assert(wide_tile_waves(kWideMaxOrder) <= 12, "the tiles layout fits 768 threads");
+
+// A wavefront's steps fall in three phases:
+//   * before its tile's block (j < c0): every entry of the tile takes the
+//     rank-1 update, the multiplier read from the slot of its own row;
+//   * inside it: the recurrence on the tile's triangle, unrolled at compile time
+//     relative to the block, publishing the next column of its rows and storing
+//     the finished one at every step;
+//   * after it: barriers only.
+// Every wavefront runs the same code, its tile decided at run time, so one
+// kernel serves every order.
+template <bool UPPER>
+__global__ __launch_bounds__(768) void potrf_wide_tiles_kernel(float* __restrict__ A, int n, int64_t lda,
+                                                               int64_t stride, int64_t batch,
+                                                               int32_t* __restrict__ info)
+{
+    constexpr int CB = kTileCols;
+    __shared__ __attribute__((aligned(16))) float colbuf[2][kWideSlots];
+
+    const int lane = threadIdx.x & 63;
+    const int q16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int rb = 0, cb = wave;
+    while (cb >= wide_col_blocks(rb, n)) {
+        cb -= wide_col_blocks(rb, n);
+        ++rb;
+    }
+    const int c0 = cb * CB;                   // first column of the tile
+    const int nstep = (n + CB - 1) / CB * CB; // steps run by every wavefront
+    const bool reports = wave == wide_tile_waves(n) - 1;   // sees every pivot below n
+    const int i = rb * 64 + lane;
+
+    for (int64_t b = blockIdx.x; b < batch; b += gridDim.x) {
+        const WideRow m{make_rsrc(A + b * stride), uint32_t(lda) * 4u};
+        // Rows at or beyond n load as zero and are never stored, and cannot
+        // reach a row below n (as in the rows layout).
+        float a[CB];
+        const int il = opaque_row(i);
+        static_for<0, CB>([&](auto cc) {
+            constexpr int c = cc;
+            a[c] = buf_load<float>(m.rs, m.off<UPPER>(il, c0 + c, n), m.col_off<UPPER>(c0 + c));
+        });
+        int32_t inf = 0;
+        if (c0 == 0) colbuf[0][i] = a[0];
+        __syncthreads();
+
+        // before the tile's block: the whole tile takes every step's update
+        for (int j = 0; j < c0; ++j) {
+            const float* col = colbuf[j & 1];
+            const float d = col[j];
+            note_pivot(inf, d, j);
+            wide_update<0, CB>(a, col, c0, q16, -(col[i] * pivot_rcp(d)));
+            if (j + 1 == c0) colbuf[(j + 1) & 1][i] = a[0];
+            __syncthreads();
+        }
+        // inside it: the triangle, relative to the block (c0 is even, so the
+        // parity of column c0 + jj is that of jj)
+        static_for<0, CB>([&](auto jc) {
+            constexpr int jj = jc;
+            const int j = c0 + jj;
+            const float* col = colbuf[jj & 1];
+            const float d = col[j];
+            note_pivot(inf, d, j);
+            float inv, rsd, sq;
+            pivot_terms(d, inv, rsd, sq);
+            if constexpr (jj + 1 < CB) {
+                wide_update<jj + 1, CB>(a, col, c0, q16, -(a[jj] * inv));
+                colbuf[(jj + 1) & 1][i] = a[jj + 1];
+            }
+            const int is = opaque_row(i);
+            const float lij = (is == j) ? sq : a[jj] * rsd;
+            buf_store<float>(m.rs, m.off<UPPER>(is, j, n), lij, m.col_off<UPPER>(j));
+            __syncthreads();
+        });
+        // after it: keep step with the other wavefronts
+        for (int j = c0 + CB; j < nstep; ++j) __syncthreads();
+
+        if (reports && lane == 0 && info != nullptr) info[b] = inf > n ? 0 : inf;
+        __syncthreads();     // colbuf is reused by the next matrix
+    }
+}
+
+// ---------------------------------------------------------------- host side
+// Orders served (fp32): above the one-wavefront windows.
+constexpr int kWideMinOrder = 65;
 
 // Every offset inside one matrix (at most (n - 1)(lda + 1) elements, which the
 // stride bounds) must fit the 31-bit buffer offsets.
 inline bool wide_layout_ok(int64_t stride) { return stride <= int64_t(0x7fffffff) / 4; }
 
-// The window (96 or 128 columns) that serves order n.
-inline int wide_window(int n) { return n <= 96 ? 96 : 128; }
+inline int wide_threads(int n) { return n <= kWideRowsMaxOrder ? 128 : 64 * wide_tile_waves(n); }
 
 inline void wide_geometry(int n, int64_t batch, Geometry& g) {
     g.family = FAM_TINY;
-    g.P = 64 * ((wide_window(n) + 63) / 64);   // lanes holding one matrix (a row each)
+    g.threads = wide_threads(n);
+    g.P = g.threads;                                         // lanes sharing one matrix
     g.R = 1;
-    g.G = 1;                                    // one matrix per workgroup
-    g.threads = g.P;
-    g.panel = 0;
+    g.G = 1;                                                 // one matrix per workgroup
+    g.panel = n <= kWideRowsMaxOrder ? 0 : kTileCols;        // columns of a tile
     g.grid = batch < kWideMaxGrid ? batch : kWideMaxGrid;
-    g.lds = int64_t(2) * (wide_window(n) == 96 ? WideShape<96>::LD : WideShape<128>::LD) * 4;
+    g.lds = int64_t(2) * kWideSlots * 4;
 }
 
-// Enqueue both windows of one triangle (instantiated by the translation unit
-// of that triangle).
+// Enqueue one triangle (instantiated by the translation unit of that triangle).
 template <bool UPPER>
 hipError_t wide_launch(int n, float* a, int64_t lda, int64_t stride, int64_t batch, int32_t* info,
                        hipStream_t s) {
     const dim3 gd((unsigned)(batch < kWideMaxGrid ? batch : kWideMaxGrid));
-    if (wide_window(n) == 96)
-        return launch(potrf_wide_kernel<96, UPPER, true>, gd, dim3(64 * WideShape<96>::NW), 0, s, a,
-                      n, lda, stride, batch, info);
-    return launch(potrf_wide_kernel<128, UPPER, true>, gd, dim3(64 * WideShape<128>::NW), 0, s, a,
-                  n, lda, stride, batch, info);
+    const dim3 bd(wide_threads(n));
+    if (n <= 96)
+        return launch(potrf_wide_rows_kernel<96, UPPER>, gd, bd, 0, s, a, n, lda, stride, batch, info);
+    if (n <= kWideRowsMaxOrder)
+        return launch(potrf_wide_rows_kernel<128, UPPER>, gd, bd, 0, s, a, n, lda, stride, batch, info);
+    return launch(potrf_wide_tiles_kernel<UPPER>, gd, bd, 0, s, a, n, lda, stride, batch, info);
 }
 
 }  // namespace wide_detail

@@ -42,6 +42,7 @@ PASS_TIMEOUT_S = 120
 # cycles of one of them.
 XCDS = 8
 SIMDS = 1024
+CUS = 256
 
 # counter groups, one rocprofv3 pass each
 def counter_passes(dt: str, family: str) -> list[list[str]]:
@@ -54,6 +55,10 @@ def counter_passes(dt: str, family: str) -> list[list[str]]:
     ]
     if family == "blocked":
         passes.append(["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F64", "GRBM_GUI_ACTIVE"])
+    if family in ("tiny", "posv_tiny"):
+        # LDS against VALU: the register windows exchange every pivot column through LDS
+        passes.append(["SQ_LDS_IDX_ACTIVE", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VALU",
+                       "SQ_WAIT_INST_LDS", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"])
     return passes
 
 
@@ -250,6 +255,16 @@ def summary_md(name, cfg, stats, kern, vals, rec, cmds) -> str:
             derived = f"address unit busy {100 * v / gui:.0f}% of GPU cycles"
         elif k == "SQ_VALU_MFMA_BUSY_CYCLES" and gui:
             derived = f"{100 * v / (gui * SIMDS):.0f}% of SIMD cycles on MFMA"
+        elif k == "SQ_LDS_IDX_ACTIVE" and gui:
+            derived = f"LDS busy {100 * v / (gui * CUS):.0f}% of CU cycles"
+        elif k == "SQ_ACTIVE_INST_VALU" and gui:
+            derived = f"VALU busy {100 * 4 * v / (gui * SIMDS):.0f}% of SIMD cycles"
+        elif k == "SQ_ACTIVE_INST_LDS" and vals.get("SQ_INSTS_LDS"):
+            derived = f"{4 * v / vals['SQ_INSTS_LDS']:.1f} cycles per LDS instruction"
+        elif k == "SQ_WAIT_INST_LDS" and vals.get("SQ_WAVE_CYCLES"):
+            derived = f"{100 * v / vals['SQ_WAVE_CYCLES']:.0f}% of wave cycles waiting to issue LDS"
+        elif k == "SQ_BUSY_CU_CYCLES" and gui:
+            derived = f"CU busy {100 * 4 * v / (gui * CUS):.0f}% of cycles"
         elif k == "GRBM_GUI_ACTIVE":
             derived = f"{v / XCDS:.0f} cycles per XCD"
         lines.append(f"| {k} | {v:.6g} | {derived} |")

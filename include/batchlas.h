@@ -91,13 +91,14 @@ typedef enum {
 /* Launch geometry chosen for a call (for tests and tracing). */
 typedef struct {
     int32_t family;             /* batchlas_family actually used                         */
-    int32_t lanes_per_matrix;   /* tiny / posv: lanes that share one matrix (P); 128 in
-                                   the wide fp32 window (orders 65..128, two wavefronts)   */
+    int32_t lanes_per_matrix;   /* tiny / posv: lanes that share one matrix (P); in the
+                                   wide fp32 window (orders 65..192) the workgroup         */
     int32_t rows_per_lane;      /* tiny / posv: rows each lane holds (R)                  */
     int32_t matrices_per_wave;  /* tiny / posv: matrices packed in one wavefront (G); 1
                                    in the wide window (one matrix per workgroup)           */
     int32_t block_threads;      /* threads per workgroup of the main kernel              */
-    int32_t panel;              /* lds / blocked: panel width (nb); 0 otherwise           */
+    int32_t panel;              /* lds / blocked: panel width (nb); wide fp32 tiles: their
+                                   column count; 0 otherwise                               */
     int64_t grid;               /* workgroups of the main kernel (first launch)          */
     int64_t lds_bytes;          /* LDS per workgroup of the main kernel                   */
 } batchlas_route_info;

@@ -120,9 +120,9 @@ def test_route_auto_picks_by_size(lib):
     # the one-matrix-per-wavefront windows end each type's tiny range; above it
     # the real types go to the blocked family, the complex ones to the LDS family
     # up to its measured cut
-    for dt, top in (("f32", 128), ("f64", 64), ("c64", 64), ("c128", 32)):
+    for dt, top in (("f32", 192), ("f64", 64), ("c64", 64), ("c128", 32)):
         assert bl.route(dt, "L", top, 16384)["family"] == "tiny"
-    for dt, n, fam in (("f32", 129, "blocked"), ("f64", 96, "blocked"), ("c64", 65, "lds"),
+    for dt, n, fam in (("f32", 193, "blocked"), ("f64", 96, "blocked"), ("c64", 65, "lds"),
                        ("c64", 96, "lds"), ("c64", 97, "blocked"), ("c128", 33, "lds"),
                        ("c128", 64, "lds"), ("c128", 65, "blocked")):
         assert bl.route(dt, "U", n, 16384)["family"] == fam, (dt, n)
@@ -209,19 +209,30 @@ def test_counter_digest_follows_the_family_sources(tmp_path, monkeypatch):
 
 
 def test_route_wide_window_geometry(lib):
-    """fp32 orders 65..128: one matrix per workgroup of two wavefronts (a row
-    per lane), the 96- or 128-column window, at most 2^20 workgroups."""
+    """fp32 orders 65..192: one matrix per workgroup.  Up to 128, two
+    wavefronts holding a row per lane; above, one wavefront per tile of 64 rows
+    x 32 columns below the diagonal.  At most 2^20 workgroups."""
+    def tile_waves(n):
+        w, rb = 0, 0
+        while 64 * rb < n:
+            w += -(-min(64 * (rb + 1), n) // 32)
+            rb += 1
+        return w
+    assert (tile_waves(129), tile_waves(160), tile_waves(192)) == (11, 11, 12)
     for uplo in ("L", "U"):
-        for n in (65, 96, 97, 128):
+        for n in (65, 96, 97, 128, 129, 160, 192):
+            threads = 128 if n <= 128 else 64 * tile_waves(n)
             for batch in (1, 1000, (1 << 20) + 5):
                 r = bl.route("f32", uplo, n, batch, family="tiny")
                 assert r["family"] == "tiny"
-                assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == (128, 1, 1)
-                assert r["block_threads"] == 128
+                assert r["block_threads"] == threads <= 768
+                assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == \
+                    (threads, 1, 1)
+                assert r["panel"] == (0 if n <= 128 else 32)
                 assert r["grid"] == min(batch, 1 << 20)
-                assert r["lds_bytes"] == 2 * (128 + 4) * 4
+                assert r["lds_bytes"] == 2 * (192 + 4) * 4
     with pytest.raises(bl.BatchlasError) as e:
-        bl.route("f32", "L", 129, 64, family="tiny")
+        bl.route("f32", "L", 193, 64, family="tiny")
     assert e.value.status_name == "NOT_SUPPORTED"
     # the layout bound: every offset of one matrix within 2^31 bytes
     with pytest.raises(bl.BatchlasError):

@@ -1,13 +1,14 @@
-"""GPU parity of the tiny family's wide fp32 window (orders 65..128, one matrix
-per workgroup of two wavefronts, a row per lane) against the CPU oracle.
+"""GPU parity of the tiny family's wide fp32 window (orders 65..192, one matrix
+per workgroup: two wavefronts holding a row per lane up to order 128, one
+wavefront per tile of 64 rows x 32 columns above) against the CPU oracle.
 
 Same bar as the other families: info bit-exact on every item, the referenced
 triangle within 1e-4 relative Frobenius error per item, the other triangle and
 the padding untouched.  The cases aim at what is particular to the window: the
-column exchange between the two wavefronts (failures and stale pivots on both
-sides of row 64), the two compile-time windows (96 and 128 columns, so orders
-96 / 97 and 128 are edges), rows beyond n inside a window, and batches beyond
-the launch's grid cap and beyond 2^31 elements.
+column exchange between wavefronts (failures and stale pivots on both sides of
+row 64, which is also a tile's edge), the change of layout above order 128,
+the two row windows (96 and 128 columns), rows and tiles partly beyond n, and
+batches beyond the launch's grid cap and beyond 2^31 elements.
 """
 from __future__ import annotations
 
@@ -47,9 +48,9 @@ def test_wide_every_order(uplo):
     """Every order of the window, both triangles, with failures planted at
     random columns in every seventh item."""
     import dense_linear_algebra_potrf_amd as bl
-    for n in range(65, 129):
-        r = bl.route("f32", uplo, n, 41)
-        assert r["family"] == "tiny" and r["block_threads"] == 128, (n, r)
+    for n in range(65, 193):
+        r = bl.route("f32", uplo, n, 41, family="tiny")
+        assert r["family"] == "tiny" and r["lanes_per_matrix"] >= 128, (n, r)
         a = syn.spd_matrices(n, 41, "f32", seed=1000 + 2 * n + (uplo == "U"))
         want = syn.plant_failures(a, seed=n, every=7)
         check_potrf(a, uplo, family="tiny", expect_info=want, label="wide-every-order")
@@ -60,7 +61,7 @@ def test_wide_poison_and_padding(uplo):
     """Padded layout (lda > n, stride > lda n) with NaN then sentinel fill in
     the padding and the unreferenced triangle: nothing there is read or
     written."""
-    for n in (65, 77, 96, 97, 120, 128):
+    for n in (65, 77, 96, 97, 120, 128, 129, 150, 160, 161, 192):
         a = syn.spd_matrices(n, 19, "f32", seed=n)
         syn.plant_failures(a, seed=n, every=5)
         for fill in (syn.nan_value("f32"), syn.sentinel("f32")):
@@ -68,12 +69,12 @@ def test_wide_poison_and_padding(uplo):
 
 
 @pytest.mark.parametrize("uplo", UPLOS)
-@pytest.mark.parametrize("n", [90, 128])
+@pytest.mark.parametrize("n", [90, 128, 160])
 def test_wide_info_first_failure_nan_and_stale_pivot(uplo, n):
-    """The first failing column wins, on either wavefront's side of row 64; a
-    NaN pivot fails; a pivot that only goes non-positive in its Schur
-    complement fails at that column, here with the chain crossing from
-    wavefront 0's rows into wavefront 1's."""
+    """The first failing column wins, on either side of row 64; a NaN pivot
+    fails; a pivot that only goes non-positive in its Schur complement fails at
+    that column, here with the chain crossing row 64 and the column block edge
+    there."""
     a = syn.spd_matrices(n, 8, "f32", seed=31 + n)
     a[0, 3, 3] *= -1
     a[0, 70, 70] *= -1                        # two plants: the first wins
@@ -90,7 +91,7 @@ def test_wide_info_first_failure_nan_and_stale_pivot(uplo, n):
     assert list(info) == [4, 1, 65, n, 66, 65, 64, 0]
 
 
-@pytest.mark.parametrize("uplo,n", [("L", 65), ("U", 128)])
+@pytest.mark.parametrize("uplo,n", [("L", 65), ("U", 128), ("L", 150)])
 def test_wide_batch_beyond_the_grid_cap_is_uniform(uplo, n):
     """More matrices than the launch's workgroups (2^20): every workgroup loops
     over several matrices.  Identical items give the solo result bit for bit,
@@ -98,14 +99,14 @@ def test_wide_batch_beyond_the_grid_cap_is_uniform(uplo, n):
     import torch
     import dense_linear_algebra_potrf_amd as bl
     batch = (1 << 20) + 5
-    r = bl.route("f32", uplo, n, batch)
-    assert r["family"] == "tiny" and r["grid"] == 1 << 20
+    r = bl.route("f32", uplo, n, batch, family="tiny")
+    assert r["grid"] == 1 << 20
     one = syn.spd_matrices(n, 1, "f32", seed=2 * n)
     solo = _replicas(one, 1)
-    bl.potrf(solo, uplo, n=n, batch=1)
+    bl.potrf(solo, uplo, n=n, batch=1, family="tiny")
     announce("wide beyond grid cap", uplo, f"n={n}", f"batch={batch}")
     many = _replicas(one, batch)
-    info = bl.potrf(many, uplo, n=n, batch=batch)
+    info = bl.potrf(many, uplo, n=n, batch=batch, family="tiny")
     torch.cuda.synchronize()
     assert int((info != 0).sum()) == 0
     assert torch.equal(_bits(many).view(batch, -1), _bits(solo).view(1, -1).expand(batch, -1))
