@@ -112,7 +112,11 @@ int auto_tiny_cut(DT dt) {
     // 899), 1.4-1.5x at 129..192 (tiles: n=129 896 against 1245, n=192 b3640 498
     // against 732); Upper alike
     case DT::F32: return 192;
-    case DT::F64: return 64;    // 64 x 1: 324 us against 438 at n=33, 342 against 2593 at n=64
+    // fp64: 64 x 1 (324 us against 438 at n=33, 342 against 2593 at n=64), then
+    // the wide window's tiles, 1.3-1.8x faster than the blocked family at 65..128
+    // (n=65 b15883 789 us against 1403, n=128 b4096 375 against 503) and slower
+    // above (n=144 731 against 578, n=192 553 against 448)
+    case DT::F64: return 128;
     case DT::C64: return 64;    // the 64 x 1 window beats the LDS family at 33..64
     case DT::C128: return 32;   // 32 x 1: 90-115 us against 321-993 at n=17..32
     }

@@ -162,8 +162,8 @@ __device__ __forceinline__ void pivot_terms(double d, double& inv, double& rs, d
 
 // ---------------------------------------------------------------- row broadcast multiply-add
 // acc += s * x, where x is `col` as held by lane N of this lane's row of 16
-// lanes: the DPP row broadcast (row_newbcast) is applied to the multiply-add's
-// first operand, so a value spread over 16 lanes feeds 16 updates of every lane
+// lanes: the DPP row broadcast (row_newbcast, also defined for 64-bit operands)
+// is applied to the multiply-add's first operand, so a value spread over 16 lanes feeds 16 updates of every lane
 // with no extra instruction.  A DPP read of a register written by a vector ALU
 // instruction needs two wait states first; FIRST (the first use of a freshly
 // loaded `col`) adds them, in case the compiler copies `col` with a vector move.
@@ -175,6 +175,17 @@ __device__ __forceinline__ void fma_bcast16(float& acc, float s, float col) {
                      : "+v"(acc) : "v"(col), "v"(s), "i"(N));
     else
         asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                     : "+v"(acc) : "v"(col), "v"(s), "i"(N));
+}
+
+template <int N, bool FIRST>
+__device__ __forceinline__ void fma_bcast16(double& acc, double s, double col) {
+    static_assert(N >= 0 && N < 16, "lane within a row of 16");
+    if constexpr (FIRST)
+        asm volatile("s_nop 1\n\tv_fmac_f64_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                     : "+v"(acc) : "v"(col), "v"(s), "i"(N));
+    else
+        asm volatile("v_fmac_f64_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
                      : "+v"(acc) : "v"(col), "v"(s), "i"(N));
 }
 

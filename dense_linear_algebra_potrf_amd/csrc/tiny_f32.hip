@@ -18,14 +18,14 @@ bool wide_order(int n) { return n > tiny_detail::last_nb(tiny_detail::TinyConfig
 int tiny_max_n_f32() { return wide_detail::kWideMaxOrder; }
 
 bool tiny_layout_ok_f32(int n, int64_t stride) {
-    if (wide_order(n)) return wide_detail::wide_layout_ok(stride);
+    if (wide_order(n)) return wide_detail::wide_layout_ok<float>(stride);
     return tiny_detail::layout_ok_t<float>(n, stride);
 }
 
 bool tiny_geometry_f32(bool upper, int n, int64_t lda, int64_t stride, int64_t batch, Geometry& g) {
     if (wide_order(n)) {
         if (n > wide_detail::kWideMaxOrder) return false;
-        wide_detail::wide_geometry(n, batch, g);
+        wide_detail::wide_geometry<float>(n, batch, g);
         return true;
     }
     return tiny_detail::geometry_t<float>(upper, n, lda, stride, batch, g);

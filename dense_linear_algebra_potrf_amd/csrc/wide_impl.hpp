@@ -1,5 +1,5 @@
-// Wide window of the tiny family (implementation header): fp32 orders 65..192,
-// one workgroup per matrix, the matrix held in the registers of several
+// Wide window of the tiny family (implementation header): fp32 and fp64 orders
+// 65..192, one workgroup per matrix, the matrix held in the registers of several
 // wavefronts.
 //
 // Prior art: the BatchLAS perf_potrf page, section "potrf: the tiny tier"
@@ -9,11 +9,12 @@
 // the register file at a useful occupancy, so the rows are spread over the
 // wavefronts of a workgroup.  Two layouts:
 //
-//   * rows (orders 65..128): two wavefronts, lane l of wavefront w holding row
-//     64 w + l whole.  A row only has columns up to its diagonal, so wavefront
+//   * rows (fp32, orders 65..128): two wavefronts, lane l of wavefront w holding
+//     row 64 w + l whole.  A row only has columns up to its diagonal, so wavefront
 //     w keeps the columns below 64 (w + 1), fixed at compile time for each
 //     wavefront's code: wavefront 0 stops updating after column 63.
-//   * tiles (orders 129..192): the part of the matrix below the diagonal cut
+//   * tiles (fp32 orders 129..192, fp64 65..192, where a whole row per lane
+//     would need 2n registers): the part of the matrix below the diagonal cut
 //     into tiles of 64 rows x 32 columns, one wavefront per tile (up to 12);
 //     lane l of the wavefront for row block rb and column block cb holds
 //     columns 32 cb .. 32 cb + 31 of row 64 rb + l.
@@ -39,13 +40,14 @@
 namespace bl {
 namespace wide_detail {
 
-constexpr int kWideRowsMaxOrder = 128;           // the rows layout serves 65..128
-constexpr int kWideMaxOrder = 192;               // the tiles layout 129..192
+constexpr int kWideRowsMaxOrder = 128;           // the rows layout serves fp32 65..128
+constexpr int kWideMaxOrder = 192;               // the tiles layout the rest, to 192
 constexpr int kTileCols = 32;                    // columns of a tile
 constexpr int kWideSlots = kWideMaxOrder + 4;    // slots of each column buffer
 constexpr int64_t kWideMaxGrid = int64_t(1) << 20;
 
-// One matrix's buffer descriptor and the offsets of its elements.
+// One matrix's buffer descriptor and the byte offsets of its elements.
+template <typename T>
 struct WideRow {
     __amdgpu_buffer_rsrc_t rs;
     uint32_t lda_b;
@@ -54,7 +56,7 @@ struct WideRow {
     // and held (spilled) for the whole factorisation.
     template <bool UPPER>
     __device__ __forceinline__ uint32_t col_off(int c) const {
-        uint32_t step = UPPER ? 4u : lda_b;
+        uint32_t step = UPPER ? uint32_t(sizeof(T)) : lda_b;
         asm volatile("" : "+s"(step) : : "memory");
         return uint32_t(c) * step;
     }
@@ -62,7 +64,8 @@ struct WideRow {
     // or beyond n and for entries above the diagonal.
     template <bool UPPER>
     __device__ __forceinline__ uint32_t off(int i, int c, int n) const {
-        return (c <= i && i < n) ? (UPPER ? uint32_t(i) * lda_b : uint32_t(i) * 4u) : kBufOOB;
+        return (c <= i && i < n) ? (UPPER ? uint32_t(i) * lda_b : uint32_t(i) * uint32_t(sizeof(T)))
+                                 : kBufOOB;
     }
 };
 
@@ -77,11 +80,11 @@ __device__ __forceinline__ int opaque_row(int i) {
 
 // Rank-1 update of a[K0..KE) with multiplier nt against the column entries
 // col[c0 + k], in groups of 16 rows with DPP row broadcasts.
-template <int K0, int KE, int N>
-__device__ __forceinline__ void wide_update(float (&a)[N], const float* col, int c0, int q16, float nt) {
+template <int K0, int KE, typename T, int N>
+__device__ __forceinline__ void wide_update(T (&a)[N], const T* col, int c0, int q16, T nt) {
     if constexpr (K0 < KE) {
         constexpr int G0 = K0 / 16, G1 = (KE + 15) / 16;
-        float cg[2];
+        T cg[2];
         cg[G0 & 1] = col[c0 + 16 * G0 + q16];
         static_for<G0, G1>([&](auto gg) {
             constexpr int g = gg;
@@ -96,8 +99,9 @@ __device__ __forceinline__ void wide_update(float (&a)[N], const float* col, int
 }
 
 // info: the first failing pivot (1-based), kept once set
-__device__ __forceinline__ void note_pivot(int32_t& inf, float d, int j) {
-    inf = (inf == 0 && !(d > 0.0f)) ? (j + 1) : inf;
+template <typename T>
+__device__ __forceinline__ void note_pivot(int32_t& inf, T d, int j) {
+    inf = (inf == 0 && !(d > T(0))) ? (j + 1) : inf;
     // taken now: sunk into the final store, the select chain would keep every
     // pivot alive across the factorisation
     asm volatile("" : "+v"(inf));
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void p
     // the whole matrix for the wavefront whose rows end at KE
     auto run = [&](auto kec, int64_t b) __attribute__((always_inline)) {
         constexpr int KE = decltype(kec)::value;
-        const WideRow m{make_rsrc(A + b * stride), uint32_t(lda) * 4u};
+        const WideRow<float> m{make_rsrc(A + b * stride), uint32_t(lda) * 4u};
         // Rows at or beyond n load as zero and are never stored; a row's update
         // only reads the column entries of rows at or above it, so their values
         // never reach a row below n.  Their first zero pivot (step n) only marks
@@ -189,13 +193,13 @@ static_assert(wide_tile_waves(kWideMaxOrder) <= 12, "the tiles layout fits 768 t
 //   * after it: barriers only.
 // Every wavefront runs the same code, its tile decided at run time, so one
 // kernel serves every order.
-template <bool UPPER>
-__global__ __launch_bounds__(768) void potrf_wide_tiles_kernel(float* __restrict__ A, int n, int64_t lda,
+template <typename T, bool UPPER>
+__global__ __launch_bounds__(768) void potrf_wide_tiles_kernel(T* __restrict__ A, int n, int64_t lda,
                                                                int64_t stride, int64_t batch,
                                                                int32_t* __restrict__ info)
 {
     constexpr int CB = kTileCols;
-    __shared__ __attribute__((aligned(16))) float colbuf[2][kWideSlots];
+    __shared__ __attribute__((aligned(16))) T colbuf[2][kWideSlots];
 
     const int lane = threadIdx.x & 63;
     const int q16 = lane & 15;
@@ -211,14 +215,14 @@ __global__ __launch_bounds__(768) void potrf_wide_tiles_kernel(float* __restrict
     const int i = rb * 64 + lane;
 
     for (int64_t b = blockIdx.x; b < batch; b += gridDim.x) {
-        const WideRow m{make_rsrc(A + b * stride), uint32_t(lda) * 4u};
+        const WideRow<T> m{make_rsrc(A + b * stride), uint32_t(lda) * uint32_t(sizeof(T))};
         // Rows at or beyond n load as zero and are never stored, and cannot
         // reach a row below n (as in the rows layout).
-        float a[CB];
+        T a[CB];
         const int il = opaque_row(i);
         static_for<0, CB>([&](auto cc) {
             constexpr int c = cc;
-            a[c] = buf_load<float>(m.rs, m.off<UPPER>(il, c0 + c, n), m.col_off<UPPER>(c0 + c));
+            a[c] = buf_load<T>(m.rs, m.template off<UPPER>(il, c0 + c, n), m.template col_off<UPPER>(c0 + c));
         });
         int32_t inf = 0;
         if (c0 == 0) colbuf[0][i] = a[0];
@@ -226,8 +230,8 @@ __global__ __launch_bounds__(768) void potrf_wide_tiles_kernel(float* __restrict
 
         // before the tile's block: the whole tile takes every step's update
         for (int j = 0; j < c0; ++j) {
-            const float* col = colbuf[j & 1];
-            const float d = col[j];
+            const T* col = colbuf[j & 1];
+            const T d = col[j];
             note_pivot(inf, d, j);
             wide_update<0, CB>(a, col, c0, q16, -(col[i] * pivot_rcp(d)));
             if (j + 1 == c0) colbuf[(j + 1) & 1][i] = a[0];
@@ -238,18 +242,18 @@ __global__ __launch_bounds__(768) void potrf_wide_tiles_kernel(float* __restrict
         static_for<0, CB>([&](auto jc) {
             constexpr int jj = jc;
             const int j = c0 + jj;
-            const float* col = colbuf[jj & 1];
-            const float d = col[j];
+            const T* col = colbuf[jj & 1];
+            const T d = col[j];
             note_pivot(inf, d, j);
-            float inv, rsd, sq;
+            T inv, rsd, sq;
             pivot_terms(d, inv, rsd, sq);
             if constexpr (jj + 1 < CB) {
                 wide_update<jj + 1, CB>(a, col, c0, q16, -(a[jj] * inv));
                 colbuf[(jj + 1) & 1][i] = a[jj + 1];
             }
             const int is = opaque_row(i);
-            const float lij = (is == j) ? sq : a[jj] * rsd;
-            buf_store<float>(m.rs, m.off<UPPER>(is, j, n), lij, m.col_off<UPPER>(j));
+            const T lij = (is == j) ? sq : a[jj] * rsd;
+            buf_store<T>(m.rs, m.template off<UPPER>(is, j, n), lij, m.template col_off<UPPER>(j));
             __syncthreads();
         });
         // after it: keep step with the other wavefronts
@@ -261,37 +265,46 @@ __global__ __launch_bounds__(768) void potrf_wide_tiles_kernel(float* __restrict
 }
 
 // ---------------------------------------------------------------- host side
-// Orders served (fp32): above the one-wavefront windows.
+// Orders served: above the one-wavefront windows.
 constexpr int kWideMinOrder = 65;
+
+// The rows layout is used for fp32 up to order 128, the tiles layout otherwise.
+template <typename T>
+inline bool wide_rows(int n) { return sizeof(T) == 4 && n <= kWideRowsMaxOrder; }
 
 // Every offset inside one matrix (at most (n - 1)(lda + 1) elements, which the
 // stride bounds) must fit the 31-bit buffer offsets.
-inline bool wide_layout_ok(int64_t stride) { return stride <= int64_t(0x7fffffff) / 4; }
+template <typename T>
+inline bool wide_layout_ok(int64_t stride) { return stride <= int64_t(0x7fffffff) / int64_t(sizeof(T)); }
 
-inline int wide_threads(int n) { return n <= kWideRowsMaxOrder ? 128 : 64 * wide_tile_waves(n); }
+template <typename T>
+inline int wide_threads(int n) { return wide_rows<T>(n) ? 128 : 64 * wide_tile_waves(n); }
 
+template <typename T>
 inline void wide_geometry(int n, int64_t batch, Geometry& g) {
     g.family = FAM_TINY;
-    g.threads = wide_threads(n);
+    g.threads = wide_threads<T>(n);
     g.P = g.threads;                                         // lanes sharing one matrix
     g.R = 1;
     g.G = 1;                                                 // one matrix per workgroup
-    g.panel = n <= kWideRowsMaxOrder ? 0 : kTileCols;        // columns of a tile
+    g.panel = wide_rows<T>(n) ? 0 : kTileCols;               // columns of a tile
     g.grid = batch < kWideMaxGrid ? batch : kWideMaxGrid;
-    g.lds = int64_t(2) * kWideSlots * 4;
+    g.lds = int64_t(2) * kWideSlots * int64_t(sizeof(T));
 }
 
-// Enqueue one triangle (instantiated by the translation unit of that triangle).
-template <bool UPPER>
-hipError_t wide_launch(int n, float* a, int64_t lda, int64_t stride, int64_t batch, int32_t* info,
+// Enqueue one element type and triangle (instantiated by its translation unit).
+template <typename T, bool UPPER>
+hipError_t wide_launch(int n, T* a, int64_t lda, int64_t stride, int64_t batch, int32_t* info,
                        hipStream_t s) {
     const dim3 gd((unsigned)(batch < kWideMaxGrid ? batch : kWideMaxGrid));
-    const dim3 bd(wide_threads(n));
-    if (n <= 96)
-        return launch(potrf_wide_rows_kernel<96, UPPER>, gd, bd, 0, s, a, n, lda, stride, batch, info);
-    if (n <= kWideRowsMaxOrder)
-        return launch(potrf_wide_rows_kernel<128, UPPER>, gd, bd, 0, s, a, n, lda, stride, batch, info);
-    return launch(potrf_wide_tiles_kernel<UPPER>, gd, bd, 0, s, a, n, lda, stride, batch, info);
+    const dim3 bd(wide_threads<T>(n));
+    if constexpr (sizeof(T) == 4) {
+        if (n <= 96)
+            return launch(potrf_wide_rows_kernel<96, UPPER>, gd, bd, 0, s, a, n, lda, stride, batch, info);
+        if (n <= kWideRowsMaxOrder)
+            return launch(potrf_wide_rows_kernel<128, UPPER>, gd, bd, 0, s, a, n, lda, stride, batch, info);
+    }
+    return launch(potrf_wide_tiles_kernel<T, UPPER>, gd, bd, 0, s, a, n, lda, stride, batch, info);
 }
 
 }  // namespace wide_detail

@@ -117,12 +117,13 @@ def test_route_auto_picks_by_size(lib):
     assert bl.route("f32", "L", 8, 1024)["family"] == "tiny"
     assert bl.route("f32", "L", 17, 32768)["family"] == "tiny"
     assert bl.route("c128", "U", 16, 64)["family"] == "tiny"
-    # the one-matrix-per-wavefront windows end each type's tiny range; above it
+    # the tiny range ends at the wide window's measured cut for the real types
+    # and at the one-matrix-per-wavefront windows for the complex ones; above it
     # the real types go to the blocked family, the complex ones to the LDS family
     # up to its measured cut
-    for dt, top in (("f32", 192), ("f64", 64), ("c64", 64), ("c128", 32)):
+    for dt, top in (("f32", 192), ("f64", 128), ("c64", 64), ("c128", 32)):
         assert bl.route(dt, "L", top, 16384)["family"] == "tiny"
-    for dt, n, fam in (("f32", 193, "blocked"), ("f64", 96, "blocked"), ("c64", 65, "lds"),
+    for dt, n, fam in (("f32", 193, "blocked"), ("f64", 129, "blocked"), ("c64", 65, "lds"),
                        ("c64", 96, "lds"), ("c64", 97, "blocked"), ("c128", 33, "lds"),
                        ("c128", 64, "lds"), ("c128", 65, "blocked")):
         assert bl.route(dt, "U", n, 16384)["family"] == fam, (dt, n)
@@ -231,9 +232,15 @@ def test_route_wide_window_geometry(lib):
                 assert r["panel"] == (0 if n <= 128 else 32)
                 assert r["grid"] == min(batch, 1 << 20)
                 assert r["lds_bytes"] == 2 * (192 + 4) * 4
-    with pytest.raises(bl.BatchlasError) as e:
-        bl.route("f32", "L", 193, 64, family="tiny")
-    assert e.value.status_name == "NOT_SUPPORTED"
+    # fp64 takes the tiles layout at every order of the window
+    for n in (65, 128, 192):
+        r = bl.route("f64", "U", n, 1000, family="tiny")
+        assert r["block_threads"] == 64 * tile_waves(n) and r["panel"] == 32
+        assert r["lds_bytes"] == 2 * (192 + 4) * 8
+    for dt in ("f32", "f64"):
+        with pytest.raises(bl.BatchlasError) as e:
+            bl.route(dt, "L", 193, 64, family="tiny")
+        assert e.value.status_name == "NOT_SUPPORTED"
     # the layout bound: every offset of one matrix within 2^31 bytes
     with pytest.raises(bl.BatchlasError):
         bl.route("f32", "L", 100, 4, family="tiny", lda=(1 << 29) // 100 + 1)

@@ -1,9 +1,10 @@
-"""GPU parity of the tiny family's wide fp32 window (orders 65..192, one matrix
-per workgroup: two wavefronts holding a row per lane up to order 128, one
-wavefront per tile of 64 rows x 32 columns above) against the CPU oracle.
+"""GPU parity of the tiny family's wide window (fp32 and fp64, orders 65..192,
+one matrix per workgroup: for fp32 up to order 128 two wavefronts holding a row
+per lane, otherwise one wavefront per tile of 64 rows x 32 columns) against the
+CPU oracle.
 
 Same bar as the other families: info bit-exact on every item, the referenced
-triangle within 1e-4 relative Frobenius error per item, the other triangle and
+triangle within 1e-4 (fp32) or 1e-11 (fp64) relative Frobenius error per item, the other triangle and
 the padding untouched.  The cases aim at what is particular to the window: the
 column exchange between wavefronts (failures and stale pivots on both sides of
 row 64, which is also a tile's edge), the change of layout above order 128,
@@ -21,6 +22,7 @@ from tests._gpu import announce, check_potrf
 pytestmark = pytest.mark.gpu
 
 UPLOS = ["L", "U"]
+DTS = ["f32", "f64"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -35,7 +37,7 @@ def _gpu():
 
 def _bits(t):
     import torch
-    return t.view(torch.int32)
+    return t.view(torch.int64) if t.element_size() == 8 else t.view(torch.int32)
 
 
 def _replicas(one: np.ndarray, batch: int):
@@ -43,43 +45,46 @@ def _replicas(one: np.ndarray, batch: int):
     return torch.from_numpy(syn.to_colmajor(one)).cuda().repeat(batch)
 
 
+@pytest.mark.parametrize("dt", DTS)
 @pytest.mark.parametrize("uplo", UPLOS)
-def test_wide_every_order(uplo):
+def test_wide_every_order(dt, uplo):
     """Every order of the window, both triangles, with failures planted at
     random columns in every seventh item."""
     import dense_linear_algebra_potrf_amd as bl
     for n in range(65, 193):
-        r = bl.route("f32", uplo, n, 41, family="tiny")
+        r = bl.route(dt, uplo, n, 41, family="tiny")
         assert r["family"] == "tiny" and r["lanes_per_matrix"] >= 128, (n, r)
-        a = syn.spd_matrices(n, 41, "f32", seed=1000 + 2 * n + (uplo == "U"))
+        a = syn.spd_matrices(n, 41, dt, seed=1000 + 2 * n + (uplo == "U"))
         want = syn.plant_failures(a, seed=n, every=7)
         check_potrf(a, uplo, family="tiny", expect_info=want, label="wide-every-order")
 
 
+@pytest.mark.parametrize("dt", DTS)
 @pytest.mark.parametrize("uplo", UPLOS)
-def test_wide_poison_and_padding(uplo):
+def test_wide_poison_and_padding(dt, uplo):
     """Padded layout (lda > n, stride > lda n) with NaN then sentinel fill in
     the padding and the unreferenced triangle: nothing there is read or
     written."""
     for n in (65, 77, 96, 97, 120, 128, 129, 150, 160, 161, 192):
-        a = syn.spd_matrices(n, 19, "f32", seed=n)
+        a = syn.spd_matrices(n, 19, dt, seed=n)
         syn.plant_failures(a, seed=n, every=5)
-        for fill in (syn.nan_value("f32"), syn.sentinel("f32")):
+        for fill in (syn.nan_value(dt), syn.sentinel(dt)):
             check_potrf(a, uplo, family="tiny", padded=True, fill=fill, label="wide-poison")
 
 
+@pytest.mark.parametrize("dt", DTS)
 @pytest.mark.parametrize("uplo", UPLOS)
 @pytest.mark.parametrize("n", [90, 128, 160])
-def test_wide_info_first_failure_nan_and_stale_pivot(uplo, n):
+def test_wide_info_first_failure_nan_and_stale_pivot(dt, uplo, n):
     """The first failing column wins, on either side of row 64; a NaN pivot
     fails; a pivot that only goes non-positive in its Schur complement fails at
     that column, here with the chain crossing row 64 and the column block edge
     there."""
-    a = syn.spd_matrices(n, 8, "f32", seed=31 + n)
+    a = syn.spd_matrices(n, 8, dt, seed=31 + n)
     a[0, 3, 3] *= -1
     a[0, 70, 70] *= -1                        # two plants: the first wins
-    a[1, 0, 0] = syn.nan_value("f32")         # NaN pivot in the first column
-    a[2, 64, 64] = syn.nan_value("f32")       # first row of the second wavefront
+    a[1, 0, 0] = syn.nan_value(dt)            # NaN pivot in the first column
+    a[2, 64, 64] = syn.nan_value(dt)          # first row of the second row block
     a[3, n - 1, n - 1] = -a[3, n - 1, n - 1]  # last column
     stale = np.eye(n)
     idx = [63, 64, 65]
@@ -91,20 +96,21 @@ def test_wide_info_first_failure_nan_and_stale_pivot(uplo, n):
     assert list(info) == [4, 1, 65, n, 66, 65, 64, 0]
 
 
-@pytest.mark.parametrize("uplo,n", [("L", 65), ("U", 128), ("L", 150)])
-def test_wide_batch_beyond_the_grid_cap_is_uniform(uplo, n):
+@pytest.mark.parametrize("dt,uplo,n", [("f32", "L", 65), ("f32", "U", 128), ("f32", "L", 150),
+                                       ("f64", "L", 65), ("f64", "U", 100)])
+def test_wide_batch_beyond_the_grid_cap_is_uniform(dt, uplo, n):
     """More matrices than the launch's workgroups (2^20): every workgroup loops
     over several matrices.  Identical items give the solo result bit for bit,
     including the last ones; compared on the device."""
     import torch
     import dense_linear_algebra_potrf_amd as bl
     batch = (1 << 20) + 5
-    r = bl.route("f32", uplo, n, batch, family="tiny")
+    r = bl.route(dt, uplo, n, batch, family="tiny")
     assert r["grid"] == 1 << 20
-    one = syn.spd_matrices(n, 1, "f32", seed=2 * n)
+    one = syn.spd_matrices(n, 1, dt, seed=2 * n)
     solo = _replicas(one, 1)
     bl.potrf(solo, uplo, n=n, batch=1, family="tiny")
-    announce("wide beyond grid cap", uplo, f"n={n}", f"batch={batch}")
+    announce("wide beyond grid cap", dt, uplo, f"n={n}", f"batch={batch}")
     many = _replicas(one, batch)
     info = bl.potrf(many, uplo, n=n, batch=batch, family="tiny")
     torch.cuda.synchronize()
@@ -114,17 +120,17 @@ def test_wide_batch_beyond_the_grid_cap_is_uniform(uplo, n):
     torch.cuda.empty_cache()
 
 
-def test_wide_batch_of_distinct_items_matches_the_oracle_at_every_sampled_item():
-    """fp32 n=128 over 8192 distinct matrices (the secondary workload's
-    shape), Lower: every item against the oracle, in chunks."""
+@pytest.mark.parametrize("dt,n,batch", [("f32", 128, 8192), ("f64", 160, 2048)])
+def test_wide_batch_of_distinct_items_matches_the_oracle_at_every_item(dt, n, batch):
+    """Thousands of distinct matrices (fp32: the secondary workload's shape),
+    Lower: every item against the oracle, in chunks."""
     import torch
     import dense_linear_algebra_potrf_amd as bl
     import oracle
     from tests._checks import TOL, rel_err_triangle
-    n, batch = 128, 8192
-    a = syn.spd_matrices(n, batch, "f32", seed=1006)
+    a = syn.spd_matrices(n, batch, dt, seed=1006)
     buf = syn.to_colmajor(a)
-    announce("wide distinct", f"n={n}", f"batch={batch}")
+    announce("wide distinct", dt, f"n={n}", f"batch={batch}")
     t = torch.from_numpy(buf).cuda()
     info = bl.potrf(t, "L", n=n, batch=batch)
     torch.cuda.synchronize()
@@ -137,4 +143,4 @@ def test_wide_batch_of_distinct_items_matches_the_oracle_at_every_sampled_item()
         got = syn.from_colmajor(out[c0 * n * n:(c0 + 512) * n * n], n, n, 512, n, n * n)
         want = syn.from_colmajor(ref, n, n, 512, n, n * n)
         worst = max(worst, float(rel_err_triangle(got, want, "L").max()))
-    assert worst <= TOL["f32"], worst
+    assert worst <= TOL[dt], worst
