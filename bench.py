@@ -46,15 +46,18 @@ CONFIGS = {
     "posv_f32_L_n32_r4_b16384": dict(op="posv", dt="f32", uplo="L", n=32, nrhs=4, batch=16384, seed=1003),
     "potrf_c64_U_n64_b16384": dict(op="potrf", dt="c64", uplo="U", n=64, batch=16384, seed=1004),
     "potrf_f64_L_n512_b1024": dict(op="potrf", dt="f64", uplo="L", n=512, batch=1024, seed=1005),
-    # beyond the listed workloads: a mid order (the blocked family at n = 128) and
-    # the complex blocked path at the largest order
+    # beyond the listed workloads: mid orders (the tiny family's wide window, one
+    # per layout) and the complex blocked path at the largest order
     "potrf_f32_L_n128_b8192": dict(op="potrf", dt="f32", uplo="L", n=128, batch=8192, seed=1006),
+    "potrf_f64_L_n96_b8192": dict(op="potrf", dt="f64", uplo="L", n=96, batch=8192, seed=1008),
+    "potrf_c64_L_n128_b4096": dict(op="potrf", dt="c64", uplo="L", n=128, batch=4096, seed=1009),
     "potrf_c64_L_n512_b1024": dict(op="potrf", dt="c64", uplo="L", n=512, batch=1024, seed=1007),
 }
 PRIMARY = "potrf_f32_L_n33_b16384"
 SECONDARY = ["potrf_f32_L_n17_b32768", "potrf_f32_L_n8_b1024", "potrf_f32_L_n8_b1048576",
              "posv_f32_L_n32_r4_b16384", "potrf_c64_U_n64_b16384", "potrf_f64_L_n512_b1024",
-             "potrf_f32_L_n128_b8192", "potrf_c64_L_n512_b1024"]
+             "potrf_f32_L_n128_b8192", "potrf_f64_L_n96_b8192", "potrf_c64_L_n128_b4096",
+             "potrf_c64_L_n512_b1024"]
 
 
 def describe(cfg: dict) -> str:
@@ -68,11 +71,11 @@ def describe(cfg: dict) -> str:
 # The sources each route's kernels are built from: a counter run stays valid
 # while these are unchanged (with no family given, every source counts).
 FAMILY_SOURCES = {
-    "tiny": ("tiny",),
+    "tiny": ("tiny", "wide"),
     "posv_tiny": ("tiny", "posv"),
     "lds": ("lds",),
     "blocked": ("blocked",),
-    "posv_split": ("tiny", "lds", "blocked", "potrs"),
+    "posv_split": ("tiny", "wide", "lds", "blocked", "potrs"),
 }
 COMMON_SOURCES = ("common.hpp", "families.hpp", "api.cpp")
 

@@ -117,8 +117,16 @@ int auto_tiny_cut(DT dt) {
     // (n=65 b15883 789 us against 1403, n=128 b4096 375 against 503) and slower
     // above (n=144 731 against 578, n=192 553 against 448)
     case DT::F64: return 128;
-    case DT::C64: return 64;    // the 64 x 1 window beats the LDS family at 33..64
-    case DT::C128: return 32;   // 32 x 1: 90-115 us against 321-993 at n=17..32
+    // cfloat: the 64 x 1 window beats the LDS family at 33..64; the wide window's
+    // tiles beat both other families at every order 65..192 (n=65 b15883 1454 us
+    // against 2900 LDS, n=128 b4096 697 against 1963 blocked, n=192 b1820 1026
+    // against 1616)
+    case DT::C64: return 192;
+    // cdouble: 32 x 1 (90-115 us against 321-993 at n=17..32), then the wide
+    // tiles at every order 33..192 (n=33 b16384 476 against 597-1020 LDS, n=64
+    // b8192 300 against 1694, n=128 b2048 638 against 1153 blocked, n=192 b910
+    // 606 against 997)
+    case DT::C128: return 192;
     }
     return 0;
 }
@@ -162,8 +170,9 @@ bool family_can_run_potrf(int fam, DT dt, int n, int64_t lda, int64_t stride) {
     return false;
 }
 
-// Largest order the dispatcher sends to the LDS family (above the tiny cut);
-// the blocked family takes everything above it.  From a sweep of the three
+// Largest order the dispatcher sends to the LDS family when the tiny family
+// cannot take the shape (a stride beyond its 31-bit offsets); the blocked
+// family takes everything above it.  From a sweep of the three
 // families on MI355X at orders 48..256 (batches of 16384 or 512 MB, both uplo,
 // us per call, LDS against blocked): the real types lose on the LDS family at
 // every order it serves above 64 (fp32 n=65 2441 against 1340, n=96 3094

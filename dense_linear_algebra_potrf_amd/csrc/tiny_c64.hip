@@ -1,19 +1,44 @@
 // Tiny-family kernels for element type cfloat (one translation unit per type so
-// the kernels build in parallel).
+// the kernels build in parallel).  Orders above the register windows run in the
+// wide window (tiles over several wavefronts), built in its own translation units.
 #include "tiny_impl.hpp"
+#include "wide_impl.hpp"
 
 namespace bl {
 
-int tiny_max_n_c64() { return tiny_detail::last_nb(tiny_detail::TinyConfigs<cfloat>::type{}); }
+hipError_t wide_potrf_c64_lower(int n, cfloat* a, int64_t lda, int64_t stride, int64_t batch,
+                                int32_t* info, hipStream_t s);
+hipError_t wide_potrf_c64_upper(int n, cfloat* a, int64_t lda, int64_t stride, int64_t batch,
+                                int32_t* info, hipStream_t s);
 
-bool tiny_layout_ok_c64(int n, int64_t stride) { return tiny_detail::layout_ok_t<cfloat>(n, stride); }
+namespace {
+bool wide_order(int n) { return n > tiny_detail::last_nb(tiny_detail::TinyConfigs<cfloat>::type{}); }
+}  // namespace
+
+int tiny_max_n_c64() { return wide_detail::kWideMaxOrder; }
+
+bool tiny_layout_ok_c64(int n, int64_t stride) {
+    if (wide_order(n)) return wide_detail::wide_layout_ok<cfloat>(stride);
+    return tiny_detail::layout_ok_t<cfloat>(n, stride);
+}
 
 bool tiny_geometry_c64(bool upper, int n, int64_t lda, int64_t stride, int64_t batch, Geometry& g) {
+    if (wide_order(n)) {
+        if (n > wide_detail::kWideMaxOrder) return false;
+        wide_detail::wide_geometry<cfloat>(n, batch, g);
+        return true;
+    }
     return tiny_detail::geometry_t<cfloat>(upper, n, lda, stride, batch, g);
 }
 
 hipError_t tiny_potrf_c64(bool upper, int n, void* A, int64_t lda, int64_t stride, int64_t batch,
                           int32_t* info, hipStream_t s) {
+    if (wide_order(n)) {
+        if (n > wide_detail::kWideMaxOrder) return hipErrorInvalidValue;
+        cfloat* a = static_cast<cfloat*>(A);
+        return upper ? wide_potrf_c64_upper(n, a, lda, stride, batch, info, s)
+                     : wide_potrf_c64_lower(n, a, lda, stride, batch, info, s);
+    }
     return tiny_detail::potrf_t<cfloat>(upper, n, A, lda, stride, batch, info, s);
 }
 

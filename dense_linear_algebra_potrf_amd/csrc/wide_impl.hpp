@@ -1,6 +1,6 @@
-// Wide window of the tiny family (implementation header): fp32 and fp64 orders
-// 65..192, one workgroup per matrix, the matrix held in the registers of several
-// wavefronts.
+// Wide window of the tiny family (implementation header): orders up to 192
+// above the one-wavefront windows (from 65; from 33 for complex double), one
+// workgroup per matrix, the matrix held in the registers of several wavefronts.
 //
 // Prior art: the BatchLAS perf_potrf page, section "potrf: the tiny tier"
 // (lane r owns row r and every value stays in registers) and section "The
@@ -13,8 +13,8 @@
 //     row 64 w + l whole.  A row only has columns up to its diagonal, so wavefront
 //     w keeps the columns below 64 (w + 1), fixed at compile time for each
 //     wavefront's code: wavefront 0 stops updating after column 63.
-//   * tiles (fp32 orders 129..192, fp64 65..192, where a whole row per lane
-//     would need 2n registers): the part of the matrix below the diagonal cut
+//   * tiles (fp32 orders 129..192, the other types throughout, where a whole
+//     row per lane would need 2n registers or more): the part below the diagonal cut
 //     into tiles of 64 rows x 32 columns, one wavefront per tile (up to 12);
 //     lane l of the wavefront for row block rb and column block cb holds
 //     columns 32 cb .. 32 cb + 31 of row 64 rb + l.
@@ -28,7 +28,10 @@
 // later.  The entries of column j a row's update needs lie in groups of 16
 // rows: lane q reads entry 16 g + (q mod 16) of group g, and each update takes
 // its row's value from the right lane of its row of 16 by a DPP broadcast
-// inside the multiply-add, so one LDS dword per lane feeds 16 updates.
+// inside the multiply-add, so one LDS read per lane feeds 16 updates.  Complex
+// elements follow the tiny family: the pivot is the real part of the diagonal,
+// the update is s_ik -= (s_ij / d) conj(s_kj), and Upper works on
+// S = conj(A^T).
 //
 // Loads and stores (Lower): lanes of a wavefront hold consecutive rows, so
 // each column is one coalesced access of 64 consecutive elements.  Upper reads
@@ -78,10 +81,35 @@ __device__ __forceinline__ int opaque_row(int i) {
     return i;
 }
 
-// Rank-1 update of a[K0..KE) with multiplier nt against the column entries
+// The multiplier of a step, as the update's multiply-adds take it: -t for the
+// real types; for the complex ones acc -= t conj(c) is
+//   acc.re += (-t.re) c.re + (-t.im) c.im,   acc.im += (-t.im) c.re + t.re c.im.
+template <typename T> struct WideMult { T n; };
+template <> struct WideMult<cfloat> { float nre, nim, tre; };
+template <> struct WideMult<cdouble> { double nre, nim, tre; };
+template <typename T>
+__device__ __forceinline__ WideMult<T> wide_mult(const T& t) {
+    if constexpr (Traits<T>::cplx) return WideMult<T>{-t.re, -t.im, t.re};
+    else return WideMult<T>{-t};
+}
+
+// acc -= t conj(x), x taken from lane N of this lane's row of 16
+template <int N, bool FIRST, typename T>
+__device__ __forceinline__ void wide_fma16(T& acc, const WideMult<T>& m, const T& col) {
+    if constexpr (Traits<T>::cplx) {
+        fma_bcast16<N, FIRST>(acc.re, m.nre, col.re);
+        fma_bcast16<N, false>(acc.re, m.nim, col.im);
+        fma_bcast16<N, false>(acc.im, m.nim, col.re);
+        fma_bcast16<N, false>(acc.im, m.tre, col.im);
+    } else {
+        fma_bcast16<N, FIRST>(acc, m.n, col);
+    }
+}
+
+// Rank-1 update of a[K0..KE) with multiplier m against the column entries
 // col[c0 + k], in groups of 16 rows with DPP row broadcasts.
 template <int K0, int KE, typename T, int N>
-__device__ __forceinline__ void wide_update(T (&a)[N], const T* col, int c0, int q16, T nt) {
+__device__ __forceinline__ void wide_update(T (&a)[N], const T* col, int c0, int q16, const WideMult<T>& m) {
     if constexpr (K0 < KE) {
         constexpr int G0 = K0 / 16, G1 = (KE + 15) / 16;
         T cg[2];
@@ -92,16 +120,16 @@ __device__ __forceinline__ void wide_update(T (&a)[N], const T* col, int c0, int
             constexpr int KB = cmax(K0, 16 * g);
             static_for<KB, cmin(KE, 16 * g + 16)>([&](auto kk) {
                 constexpr int k = kk;
-                fma_bcast16<k - 16 * g, k == KB>(a[k], nt, cg[g & 1]);
+                wide_fma16<k - 16 * g, k == KB>(a[k], m, cg[g & 1]);
             });
         });
     }
 }
 
 // info: the first failing pivot (1-based), kept once set
-template <typename T>
-__device__ __forceinline__ void note_pivot(int32_t& inf, T d, int j) {
-    inf = (inf == 0 && !(d > T(0))) ? (j + 1) : inf;
+template <typename R>
+__device__ __forceinline__ void note_pivot(int32_t& inf, R d, int j) {
+    inf = (inf == 0 && !(d > R(0))) ? (j + 1) : inf;
     // taken now: sunk into the final store, the select chain would keep every
     // pivot alive across the factorisation
     asm volatile("" : "+v"(inf));
@@ -151,7 +179,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void p
                     a[j + 1] = fmadd(-t, col[j + 1], a[j + 1]);
                     colbuf[(j + 1) & 1][i] = a[j + 1];
                 }
-                wide_update<j + 2, KE>(a, col, 0, q16, -t);
+                wide_update<j + 2, KE>(a, col, 0, q16, WideMult<float>{-t});
                 // column j is final: to the matrix now (one coalesced column),
                 // which frees its register for the rest of the factorisation
                 const int is = opaque_row(i);
@@ -198,6 +226,7 @@ __global__ __launch_bounds__(768) void potrf_wide_tiles_kernel(T* __restrict__ A
                                                                int64_t stride, int64_t batch,
                                                                int32_t* __restrict__ info)
 {
+    using R = typename Traits<T>::R;
     constexpr int CB = kTileCols;
     __shared__ __attribute__((aligned(16))) T colbuf[2][kWideSlots];
 
@@ -217,12 +246,14 @@ __global__ __launch_bounds__(768) void potrf_wide_tiles_kernel(T* __restrict__ A
     for (int64_t b = blockIdx.x; b < batch; b += gridDim.x) {
         const WideRow<T> m{make_rsrc(A + b * stride), uint32_t(lda) * uint32_t(sizeof(T))};
         // Rows at or beyond n load as zero and are never stored, and cannot
-        // reach a row below n (as in the rows layout).
+        // reach a row below n (as in the rows layout).  Upper holds
+        // S(i, c) = conj(A(c, i)): conjugated on the way in and out.
         T a[CB];
         const int il = opaque_row(i);
         static_for<0, CB>([&](auto cc) {
             constexpr int c = cc;
-            a[c] = buf_load<T>(m.rs, m.template off<UPPER>(il, c0 + c, n), m.template col_off<UPPER>(c0 + c));
+            const T v = buf_load<T>(m.rs, m.template off<UPPER>(il, c0 + c, n), m.template col_off<UPPER>(c0 + c));
+            a[c] = UPPER ? conj(v) : v;
         });
         int32_t inf = 0;
         if (c0 == 0) colbuf[0][i] = a[0];
@@ -231,9 +262,9 @@ __global__ __launch_bounds__(768) void potrf_wide_tiles_kernel(T* __restrict__ A
         // before the tile's block: the whole tile takes every step's update
         for (int j = 0; j < c0; ++j) {
             const T* col = colbuf[j & 1];
-            const T d = col[j];
+            const R d = re(col[j]);
             note_pivot(inf, d, j);
-            wide_update<0, CB>(a, col, c0, q16, -(col[i] * pivot_rcp(d)));
+            wide_update<0, CB>(a, col, c0, q16, wide_mult(scale(col[i], pivot_rcp(d))));
             if (j + 1 == c0) colbuf[(j + 1) & 1][i] = a[0];
             __syncthreads();
         }
@@ -243,17 +274,18 @@ __global__ __launch_bounds__(768) void potrf_wide_tiles_kernel(T* __restrict__ A
             constexpr int jj = jc;
             const int j = c0 + jj;
             const T* col = colbuf[jj & 1];
-            const T d = col[j];
+            const R d = re(col[j]);
             note_pivot(inf, d, j);
-            T inv, rsd, sq;
+            R inv, rsd, sq;
             pivot_terms(d, inv, rsd, sq);
             if constexpr (jj + 1 < CB) {
-                wide_update<jj + 1, CB>(a, col, c0, q16, -(a[jj] * inv));
+                wide_update<jj + 1, CB>(a, col, c0, q16, wide_mult(scale(a[jj], inv)));
                 colbuf[(jj + 1) & 1][i] = a[jj + 1];
             }
             const int is = opaque_row(i);
-            const T lij = (is == j) ? sq : a[jj] * rsd;
-            buf_store<T>(m.rs, m.template off<UPPER>(is, j, n), lij, m.template col_off<UPPER>(j));
+            const T lij = select(is == j, diag_value<T>(sq, UPPER), scale(a[jj], rsd));
+            buf_store<T>(m.rs, m.template off<UPPER>(is, j, n), UPPER ? conj(lij) : lij,
+                         m.template col_off<UPPER>(j));
             __syncthreads();
         });
         // after it: keep step with the other wavefronts
@@ -270,7 +302,7 @@ constexpr int kWideMinOrder = 65;
 
 // The rows layout is used for fp32 up to order 128, the tiles layout otherwise.
 template <typename T>
-inline bool wide_rows(int n) { return sizeof(T) == 4 && n <= kWideRowsMaxOrder; }
+inline bool wide_rows(int n) { return std::is_same<T, float>::value && n <= kWideRowsMaxOrder; }
 
 // Every offset inside one matrix (at most (n - 1)(lda + 1) elements, which the
 // stride bounds) must fit the 31-bit buffer offsets.
@@ -298,7 +330,7 @@ hipError_t wide_launch(int n, T* a, int64_t lda, int64_t stride, int64_t batch, 
                        hipStream_t s) {
     const dim3 gd((unsigned)(batch < kWideMaxGrid ? batch : kWideMaxGrid));
     const dim3 bd(wide_threads<T>(n));
-    if constexpr (sizeof(T) == 4) {
+    if constexpr (std::is_same<T, float>::value) {
         if (n <= 96)
             return launch(potrf_wide_rows_kernel<96, UPPER>, gd, bd, 0, s, a, n, lda, stride, batch, info);
         if (n <= kWideRowsMaxOrder)

@@ -107,6 +107,9 @@ def test_route_tiny_geometry_invariants(lib):
                 assert e.status_name == "NOT_SUPPORTED"
                 continue
             P, R, G = r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]
+            if P > 64:      # the wide window: one matrix over several wavefronts
+                assert dt == "c128" and n == 33 and G == 1 and P == r["block_threads"]
+                continue
             # up to 64 // P matrices per wavefront (fewer where measured faster)
             assert P * R >= n and 1 <= G <= 64 // P
             assert r["grid"] * G * (r["block_threads"] // 64) >= 1000
@@ -117,20 +120,20 @@ def test_route_auto_picks_by_size(lib):
     assert bl.route("f32", "L", 8, 1024)["family"] == "tiny"
     assert bl.route("f32", "L", 17, 32768)["family"] == "tiny"
     assert bl.route("c128", "U", 16, 64)["family"] == "tiny"
-    # the tiny range ends at the wide window's measured cut for the real types
-    # and at the one-matrix-per-wavefront windows for the complex ones; above it
-    # the real types go to the blocked family, the complex ones to the LDS family
-    # up to its measured cut
-    for dt, top in (("f32", 192), ("f64", 128), ("c64", 64), ("c128", 32)):
+    # the tiny range (with its wide window) ends at the measured cut of each type;
+    # the blocked family takes the orders above it
+    for dt, top in (("f32", 192), ("f64", 128), ("c64", 192), ("c128", 192)):
         assert bl.route(dt, "L", top, 16384)["family"] == "tiny"
-    for dt, n, fam in (("f32", 193, "blocked"), ("f64", 129, "blocked"), ("c64", 65, "lds"),
-                       ("c64", 96, "lds"), ("c64", 97, "blocked"), ("c128", 33, "lds"),
-                       ("c128", 64, "lds"), ("c128", 65, "blocked")):
-        assert bl.route(dt, "U", n, 16384)["family"] == fam, (dt, n)
-    # above the LDS family's capacity the complex types go to the blocked family
-    assert bl.route("c64", "U", 128, 64)["family"] == "blocked"
+        assert bl.route(dt, "U", top + 1, 16384)["family"] == "blocked", dt
+    for dt, n in (("c64", 65), ("c64", 96), ("c128", 33), ("c128", 64), ("c128", 65)):
+        assert bl.route(dt, "U", n, 16384)["family"] == "tiny", (dt, n)
     assert bl.route("c64", "L", 512, 64)["family"] == "blocked"
     assert bl.route("c128", "L", 256, 64)["family"] == "blocked"
+    # a stride beyond the tiny family's 31-bit offsets goes to the LDS family up
+    # to its cut (64 for cdouble), then to the blocked family
+    big = (1 << 31) // 16 + 1
+    assert bl.route("c128", "L", 40, 4, stride=big)["family"] == "lds"
+    assert bl.route("c128", "L", 65, 4, stride=big)["family"] == "blocked"
 
 
 def test_posv_auto_routes_beyond_the_window_to_split(lib):
@@ -237,7 +240,13 @@ def test_route_wide_window_geometry(lib):
         r = bl.route("f64", "U", n, 1000, family="tiny")
         assert r["block_threads"] == 64 * tile_waves(n) and r["panel"] == 32
         assert r["lds_bytes"] == 2 * (192 + 4) * 8
-    for dt in ("f32", "f64"):
+    for n in (65, 192):
+        r = bl.route("c64", "L", n, 1000, family="tiny")
+        assert r["block_threads"] == 64 * tile_waves(n) and r["lds_bytes"] == 2 * (192 + 4) * 8
+    for n in (33, 64, 65, 192):
+        r = bl.route("c128", "L", n, 1000, family="tiny")
+        assert r["block_threads"] == 64 * tile_waves(n) and r["lds_bytes"] == 2 * (192 + 4) * 16
+    for dt in ("f32", "f64", "c64", "c128"):
         with pytest.raises(bl.BatchlasError) as e:
             bl.route(dt, "L", 193, 64, family="tiny")
         assert e.value.status_name == "NOT_SUPPORTED"

@@ -1,10 +1,11 @@
-"""GPU parity of the tiny family's wide window (fp32 and fp64, orders 65..192,
+"""GPU parity of the tiny family's wide window (every type, orders 65..192, and
+33..64 for cdouble,
 one matrix per workgroup: for fp32 up to order 128 two wavefronts holding a row
 per lane, otherwise one wavefront per tile of 64 rows x 32 columns) against the
 CPU oracle.
 
 Same bar as the other families: info bit-exact on every item, the referenced
-triangle within 1e-4 (fp32) or 1e-11 (fp64) relative Frobenius error per item, the other triangle and
+triangle within 1e-4 (fp32, cfloat) or 1e-11 (fp64, cdouble) relative Frobenius error per item, the other triangle and
 the padding untouched.  The cases aim at what is particular to the window: the
 column exchange between wavefronts (failures and stale pivots on both sides of
 row 64, which is also a tile's edge), the change of layout above order 128,
@@ -22,7 +23,12 @@ from tests._gpu import announce, check_potrf
 pytestmark = pytest.mark.gpu
 
 UPLOS = ["L", "U"]
-DTS = ["f32", "f64"]
+DTS = ["f32", "f64", "c64", "c128"]
+
+
+def lowest(dt):
+    """The first order of the wide window (above the one-wavefront windows)."""
+    return 33 if dt == "c128" else 65
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -37,7 +43,7 @@ def _gpu():
 
 def _bits(t):
     import torch
-    return t.view(torch.int64) if t.element_size() == 8 else t.view(torch.int32)
+    return t.view(torch.int64) if t.element_size() >= 8 or t.is_complex() else t.view(torch.int32)
 
 
 def _replicas(one: np.ndarray, batch: int):
@@ -51,7 +57,7 @@ def test_wide_every_order(dt, uplo):
     """Every order of the window, both triangles, with failures planted at
     random columns in every seventh item."""
     import dense_linear_algebra_potrf_amd as bl
-    for n in range(65, 193):
+    for n in range(lowest(dt), 193):
         r = bl.route(dt, uplo, n, 41, family="tiny")
         assert r["family"] == "tiny" and r["lanes_per_matrix"] >= 128, (n, r)
         a = syn.spd_matrices(n, 41, dt, seed=1000 + 2 * n + (uplo == "U"))
@@ -65,7 +71,7 @@ def test_wide_poison_and_padding(dt, uplo):
     """Padded layout (lda > n, stride > lda n) with NaN then sentinel fill in
     the padding and the unreferenced triangle: nothing there is read or
     written."""
-    for n in (65, 77, 96, 97, 120, 128, 129, 150, 160, 161, 192):
+    for n in ((33, 40, 64) if dt == "c128" else ()) + (65, 77, 96, 97, 120, 128, 129, 150, 160, 161, 192):
         a = syn.spd_matrices(n, 19, dt, seed=n)
         syn.plant_failures(a, seed=n, every=5)
         for fill in (syn.nan_value(dt), syn.sentinel(dt)):
@@ -97,7 +103,8 @@ def test_wide_info_first_failure_nan_and_stale_pivot(dt, uplo, n):
 
 
 @pytest.mark.parametrize("dt,uplo,n", [("f32", "L", 65), ("f32", "U", 128), ("f32", "L", 150),
-                                       ("f64", "L", 65), ("f64", "U", 100)])
+                                       ("f64", "L", 65), ("f64", "U", 100), ("c64", "U", 80),
+                                       ("c128", "L", 40)])
 def test_wide_batch_beyond_the_grid_cap_is_uniform(dt, uplo, n):
     """More matrices than the launch's workgroups (2^20): every workgroup loops
     over several matrices.  Identical items give the solo result bit for bit,
@@ -120,7 +127,8 @@ def test_wide_batch_beyond_the_grid_cap_is_uniform(dt, uplo, n):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("dt,n,batch", [("f32", 128, 8192), ("f64", 160, 2048)])
+@pytest.mark.parametrize("dt,n,batch", [("f32", 128, 8192), ("f64", 160, 2048), ("c64", 128, 2048),
+                                         ("c128", 96, 1024)])
 def test_wide_batch_of_distinct_items_matches_the_oracle_at_every_item(dt, n, batch):
     """Thousands of distinct matrices (fp32: the secondary workload's shape),
     Lower: every item against the oracle, in chunks."""
