@@ -264,7 +264,7 @@ def summary_md(name, cfg, stats, kern, vals, rec, cmds) -> str:
         elif k == "SQ_WAIT_INST_LDS" and vals.get("SQ_WAVE_CYCLES"):
             derived = f"{100 * v / vals['SQ_WAVE_CYCLES']:.0f}% of wave cycles waiting to issue LDS"
         elif k == "SQ_BUSY_CU_CYCLES" and gui:
-            derived = f"CU busy {100 * 4 * v / (gui * CUS):.0f}% of cycles"
+            derived = f"CU busy {100 * v / (gui * CUS):.0f}% of cycles"
         elif k == "GRBM_GUI_ACTIVE":
             derived = f"{v / XCDS:.0f} cycles per XCD"
         lines.append(f"| {k} | {v:.6g} | {derived} |")

@@ -1,16 +1,16 @@
-"""GPU parity of the tiny family's wide window (every type, orders 65..192, and
-33..64 for cdouble,
-one matrix per workgroup: for fp32 up to order 128 two wavefronts holding a row
-per lane, otherwise one wavefront per tile of 64 rows x 32 columns) against the
-CPU oracle.
+"""GPU parity of the tiny family's wide window against the CPU oracle: every
+type at orders 65..192 (33..192 for cdouble), one matrix per workgroup; fp32
+up to order 128 on two wavefronts holding a row per lane, otherwise one
+wavefront per tile of 64 rows x 32 columns.
 
 Same bar as the other families: info bit-exact on every item, the referenced
-triangle within 1e-4 (fp32, cfloat) or 1e-11 (fp64, cdouble) relative Frobenius error per item, the other triangle and
-the padding untouched.  The cases aim at what is particular to the window: the
-column exchange between wavefronts (failures and stale pivots on both sides of
-row 64, which is also a tile's edge), the change of layout above order 128,
-the two row windows (96 and 128 columns), rows and tiles partly beyond n, and
-batches beyond the launch's grid cap and beyond 2^31 elements.
+triangle within 1e-4 (fp32, cfloat) or 1e-11 (fp64, cdouble) relative
+Frobenius error per item, the other triangle and the padding untouched.  The
+cases aim at what is particular to the window: the column exchange between
+wavefronts (failures and stale pivots on both sides of row 64, which is also a
+tile's edge), the change of layout above order 128, the two row windows (96
+and 128 columns), rows and tiles partly beyond n, and batches beyond the
+launch's grid cap and beyond 2^31 elements.
 """
 from __future__ import annotations
 
@@ -71,7 +71,8 @@ def test_wide_poison_and_padding(dt, uplo):
     """Padded layout (lda > n, stride > lda n) with NaN then sentinel fill in
     the padding and the unreferenced triangle: nothing there is read or
     written."""
-    for n in ((33, 40, 64) if dt == "c128" else ()) + (65, 77, 96, 97, 120, 128, 129, 150, 160, 161, 192):
+    orders = (65, 77, 96, 97, 120, 128, 129, 150, 160, 161, 192)
+    for n in ((33, 40, 64) if dt == "c128" else ()) + orders:
         a = syn.spd_matrices(n, 19, dt, seed=n)
         syn.plant_failures(a, seed=n, every=5)
         for fill in (syn.nan_value(dt), syn.sentinel(dt)):
