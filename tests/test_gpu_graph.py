@@ -14,6 +14,7 @@ from tests._gpu import announce, torch_dtype
 pytestmark = pytest.mark.gpu
 
 CASES = [("f32", "L", 33, 4096, "tiny"), ("c64", "U", 64, 512, "tiny"),
+         ("f32", "L", 128, 2048, "tiny"), ("c64", "U", 160, 256, "tiny"),
          ("f32", "U", 48, 300, "lds"), ("f64", "L", 300, 40, "blocked")]
 
 

@@ -76,8 +76,8 @@ def test_config_posv_fp32_n32_nrhs4_planted():
 # ---------------------------------------------------------------- split route
 # potrf by the dispatcher's family, then both triangular solves in one launch:
 # posv for orders and right-hand-side counts beyond the fused window.
-SPLIT_CASES = [(1, 1), (5, 6), (17, 3), (32, 5), (33, 4), (64, 9), (100, 2), (129, 5), (257, 3),
-               (512, 1)]
+SPLIT_CASES = [(1, 1), (5, 6), (17, 3), (32, 5), (33, 4), (64, 9), (100, 2), (129, 5), (192, 4),
+               (257, 3), (512, 1)]
 
 
 def split_runnable(dt, n, nrhs):
@@ -111,12 +111,14 @@ def test_posv_split_padded_layout(dt):
 
 
 @pytest.mark.parametrize("dt", ["f32", "c64"])
-def test_posv_split_without_info_matches(dt):
+@pytest.mark.parametrize("n", [45, 100])
+def test_posv_split_without_info_matches(dt, n):
     """info NULL: the solve reads failures off the factor's diagonal; X and the
-    factor must equal the run with info, bit for bit."""
+    factor must equal the run with info, bit for bit (n = 100: the wide
+    window's factor, rows layout for fp32 and tiles for cfloat)."""
     import torch
     import dense_linear_algebra_potrf_amd as bl
-    n, nrhs, batch = 45, 6, 64
+    nrhs, batch = 6, 64
     a = syn.spd_matrices(n, batch, dt, seed=77)
     syn.plant_failures(a, seed=77, every=5)
     b = syn.rhs(n, nrhs, batch, dt, seed=78)
