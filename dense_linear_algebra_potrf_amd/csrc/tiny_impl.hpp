@@ -92,15 +92,26 @@ __device__ __forceinline__ void tiny_solves(const T (&a)[R][P * R], const typena
         constexpr int rp = pv / P;
         uint32_t* row = ldsw + (pv & 1) * parity_words + p * roww;
         const bool owner = q == pv % P;
-        static_for<0, NRHS>([&](auto kk) {
-            constexpr int k = kk;
-            const T v = scale(y[rp][k], invd[rp]);
-            yf[rp][k] = select(owner, v, yf[rp][k]);
-            if (owner) lds_put<T>(row, NB + 1 + k, v);
-        });
-        wave_lds_sync();
         T yp[NRHS];
-        static_for<0, NRHS>([&](auto kk) { yp[kk] = lds_get<T>(row, NB + 1 + kk); });
+        if constexpr (P == 16 && std::is_same<T, float>::value) {
+            // a partition is one DPP row: the owner's value by a row broadcast
+            static_for<0, NRHS>([&](auto kk) {
+                constexpr int k = kk;
+                const T v = scale(y[rp][k], invd[rp]);
+                yf[rp][k] = select(owner, v, yf[rp][k]);
+                yp[k] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                    0, __builtin_bit_cast(int, v), 0x150 + (pv % 16), 0xf, 0xf, false));
+            });
+        } else {
+            static_for<0, NRHS>([&](auto kk) {
+                constexpr int k = kk;
+                const T v = scale(y[rp][k], invd[rp]);
+                yf[rp][k] = select(owner, v, yf[rp][k]);
+                if (owner) lds_put<T>(row, NB + 1 + k, v);
+            });
+            wave_lds_sync();
+            static_for<0, NRHS>([&](auto kk) { yp[kk] = lds_get<T>(row, NB + 1 + kk); });
+        }
         static_for<rp, R>([&](auto rr) {
             constexpr int r = rr;
             static_for<0, NRHS>([&](auto kk) {
@@ -270,6 +281,66 @@ __device__ __forceinline__ void factor_rows(T (&a)[R][P * R], typename Traits<T>
         });
     });
 
+}
+
+// The same recurrence for fp32 partitions of exactly 16 lanes (P = 16): a
+// partition is one DPP row, so the entry of row k = k' + 16 r of column j sits
+// in register a[r][j] of lane k' of the same row and reaches every lane of the
+// matrix by a DPP row broadcast: the pivot by a broadcast move, every update
+// by a broadcast inside its multiply-add.  No LDS exchange, so no round trip
+// per step.  Register slots right of a row's diagonal are scratch, as in
+// factor_rows.
+template <typename T, int R, bool UPPER, int NRHS, bool ONE_RSQ>
+__device__ __forceinline__ void factor_rows_dpp(T (&a)[R][16 * R], float (&invd)[R], int q, int32_t& inf)
+{
+    static_assert(std::is_same<T, float>::value, "fp32 partitions of 16 lanes");
+    constexpr int NB = 16 * R;
+    inf = 0;
+    static_for<0, R>([&](auto rr) { invd[rr] = 1.0f; });
+    static_for<0, NB>([&](auto jj) {
+        constexpr int j = jj;
+        constexpr int rj = j / 16;
+        const float d = __builtin_bit_cast(
+            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a[rj][j]), 0x150 + (j % 16), 0xf,
+                                               0xf, false));
+        inf = (inf == 0 && !(d > 0.0f)) ? (j + 1) : inf;
+        float inv, rs, sq;
+        step_pivot<ONE_RSQ>(d, inv, rs, sq);
+        float nt[R];
+        static_for<rj, R>([&](auto rr) {
+            constexpr int r = rr;
+            nt[r] = -(a[r][j] * inv);
+        });
+        // column j + 1 first (the next pivot's entry), then the rest
+        if constexpr (j + 1 < NB) {
+            constexpr int k = j + 1;
+            static_for<k / 16, R>([&](auto rr) {
+                constexpr int r = rr;
+                fma_bcast16<k % 16, r == k / 16>(a[r][k], nt[r], a[k / 16][j]);
+            });
+        }
+        static_for<rj, R>([&](auto rr) {
+            constexpr int r = rr;
+            constexpr int kend = cmin(NB, (r + 1) * 16);
+            static_for<j + 2, kend>([&](auto kk) {
+                constexpr int k = kk;
+                // (wait states before the first read of each source register)
+                fma_bcast16<k % 16, k == j + 2 || k % 16 == 0>(a[r][k], nt[r], a[k / 16][j]);
+            });
+        });
+        // column j is the broadcast source of every row block's updates, so it
+        // is scaled only once they are all issued
+        static_for<rj, R>([&](auto rr) {
+            constexpr int r = rr;
+            if constexpr (r == rj) {
+                const bool diag = (q + r * 16) == j;
+                a[r][j] = diag ? diag_value<T>(sq, UPPER) : a[r][j] * rs;
+                if constexpr (NRHS > 0) invd[r] = diag ? rs : invd[r];
+            } else {
+                a[r][j] = a[r][j] * rs;
+            }
+        });
+    });
 }
 
 // The same recurrence with one matrix per wavefront (P = 64, R = 1: lane i
@@ -601,6 +672,8 @@ __global__ __launch_bounds__(PACKED ? 64 : 64 * kTinyWaves) void potrf_tiny_kern
     constexpr bool ONE_RSQ = one_rsq_window<T, P, R, NRHS>();
     if constexpr (P == 64 && R == 1)
         factor_rows_lane<T, UPPER, NRHS, ROWW, ONE_RSQ>(a, invd, xbuf, q, inf);
+    else if constexpr (P == 16 && std::is_same<T, float>::value)
+        factor_rows_dpp<T, R, UPPER, NRHS, ONE_RSQ>(a, invd, q, inf);
     else
         factor_rows<T, P, R, UPPER, NRHS, ROWW, ONE_RSQ>(a, invd, xbuf, p, q, inf);
 
