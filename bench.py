@@ -71,11 +71,11 @@ def describe(cfg: dict) -> str:
 # The sources each route's kernels are built from: a counter run stays valid
 # while these are unchanged (with no family given, every source counts).
 FAMILY_SOURCES = {
-    "tiny": ("tiny", "wide"),
+    "tiny": ("tiny", "wide", "fold"),
     "posv_tiny": ("tiny", "posv"),
     "lds": ("lds",),
     "blocked": ("blocked",),
-    "posv_split": ("tiny", "wide", "lds", "blocked", "potrs"),
+    "posv_split": ("tiny", "wide", "fold", "lds", "blocked", "potrs"),
 }
 COMMON_SOURCES = ("common.hpp", "families.hpp", "api.cpp")
 

@@ -1,8 +1,11 @@
 // Tiny-family kernels for element type double (one translation unit per type so
-// the kernels build in parallel).  Orders above the register windows run in the
-// wide window (tiles over several wavefronts), built in its own translation units.
+// the kernels build in parallel).  Orders 33..64 run in the folded window (two
+// matrices per wavefront, a short and a long row per lane), orders above the
+// register windows in the wide window (tiles over several wavefronts); both are
+// built in translation units of their own.
 #include "tiny_impl.hpp"
 #include "wide_impl.hpp"
+#include "fold_impl.hpp"
 
 namespace bl {
 
@@ -10,15 +13,23 @@ hipError_t wide_potrf_f64_lower(int n, double* a, int64_t lda, int64_t stride, i
                                 int32_t* info, hipStream_t s);
 hipError_t wide_potrf_f64_upper(int n, double* a, int64_t lda, int64_t stride, int64_t batch,
                                 int32_t* info, hipStream_t s);
+hipError_t fold_potrf_f64(bool upper, int n, double* a, int64_t lda, int64_t stride, int64_t batch,
+                          int32_t* info, hipStream_t s);
 
 namespace {
 bool wide_order(int n) { return n > tiny_detail::last_nb(tiny_detail::TinyConfigs<double>::type{}); }
+// orders 33..64 in the folded window where a pair of matrices fits its 31-bit
+// offsets (else the one-wavefront window)
+bool use_fold(int n, int64_t stride) {
+    return n >= fold_detail::kFoldMin && n <= fold_detail::kFoldMax && fold_detail::fold_layout_ok<double>(stride);
+}
 }  // namespace
 
 int tiny_max_n_f64() { return wide_detail::kWideMaxOrder; }
 
 bool tiny_layout_ok_f64(int n, int64_t stride) {
     if (wide_order(n)) return wide_detail::wide_layout_ok<double>(stride);
+    if (use_fold(n, stride)) return true;
     return tiny_detail::layout_ok_t<double>(n, stride);
 }
 
@@ -26,6 +37,10 @@ bool tiny_geometry_f64(bool upper, int n, int64_t lda, int64_t stride, int64_t b
     if (wide_order(n)) {
         if (n > wide_detail::kWideMaxOrder) return false;
         wide_detail::wide_geometry<double>(n, batch, g);
+        return true;
+    }
+    if (use_fold(n, stride)) {
+        fold_detail::fold_geometry<double>(upper, batch, g);
         return true;
     }
     return tiny_detail::geometry_t<double>(upper, n, lda, stride, batch, g);
@@ -39,6 +54,7 @@ hipError_t tiny_potrf_f64(bool upper, int n, void* A, int64_t lda, int64_t strid
         return upper ? wide_potrf_f64_upper(n, a, lda, stride, batch, info, s)
                      : wide_potrf_f64_lower(n, a, lda, stride, batch, info, s);
     }
+    if (use_fold(n, stride)) return fold_potrf_f64(upper, n, static_cast<double*>(A), lda, stride, batch, info, s);
     return tiny_detail::potrf_t<double>(upper, n, A, lda, stride, batch, info, s);
 }
 

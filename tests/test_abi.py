@@ -255,6 +255,35 @@ def test_route_wide_window_geometry(lib):
         bl.route("f32", "L", 100, 4, family="tiny", lda=(1 << 29) // 100 + 1)
 
 
+def test_route_folded_window_geometry(lib):
+    """fp64 and cfloat orders 33..64: two matrices per wavefront, 32 lanes x 2
+    rows each (rows q and 63 - q), one wavefront per workgroup, a grid of pairs
+    capped at 2^19; Upper adds the slab tile to the pivot buffers.  A stride
+    whose pair of matrices leaves the 31-bit offsets falls back to the
+    one-wavefront window; fp32 keeps that window at these orders."""
+    for dt, es in (("f64", 8), ("c64", 8)):
+        for uplo in ("L", "U"):
+            for n in (33, 40, 63, 64):
+                for batch in (1, 2, 1001, (1 << 20) + 5):
+                    r = bl.route(dt, uplo, n, batch)
+                    assert r["family"] == "tiny", (dt, n)
+                    assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == \
+                        (32, 2, 2)
+                    assert r["block_threads"] == 64
+                    assert r["grid"] == min((batch + 1) // 2, 1 << 19)
+                    lds = 2 * 2 * 68 * es + (2 * 64 * (128 // es + 1) * es if uplo == "U" else 0)
+                    assert r["lds_bytes"] == lds
+        top = (1 << 31) // es // 2                  # largest stride whose pair fits, with margin
+        assert bl.route(dt, "L", 40, 4, stride=top - 1)["lanes_per_matrix"] == 32
+        r = bl.route(dt, "L", 40, 4, stride=top + 64)
+        assert r["family"] == "tiny" and r["lanes_per_matrix"] == 64 and r["matrices_per_wave"] == 1
+    # the neighbours: order 32 in a smaller register window, 65 in the wide window
+    assert bl.route("f64", "L", 32, 1000)["matrices_per_wave"] > 2
+    assert bl.route("f64", "L", 65, 1000)["block_threads"] > 64
+    for n in (34, 48, 64):
+        assert bl.route("f32", "L", n, 1000)["lanes_per_matrix"] == 64
+
+
 def test_tiny_grid_is_capped_for_huge_batches(lib):
     """A batch of 2^30 matrices of order 4 (16 per wavefront) would need 2^26
     one-wavefront workgroups; the tiny family launches it in slices of at most
