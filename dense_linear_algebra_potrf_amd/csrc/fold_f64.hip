@@ -6,8 +6,8 @@ namespace bl {
 
 hipError_t fold_potrf_f64(bool upper, int n, double* a, int64_t lda, int64_t stride, int64_t batch,
                           int32_t* info, hipStream_t s) {
-    return upper ? fold_detail::fold_launch<double, true>(n, a, lda, stride, batch, info, s)
-                 : fold_detail::fold_launch<double, false>(n, a, lda, stride, batch, info, s);
+    return upper ? fold_detail::fold_launch<double, 64, true>(n, a, lda, stride, batch, info, s)
+                 : fold_detail::fold_launch<double, 64, false>(n, a, lda, stride, batch, info, s);
 }
 
 }  // namespace bl

@@ -3,6 +3,7 @@
 // wide window (two wavefronts per matrix), built in its own translation units.
 #include "tiny_impl.hpp"
 #include "wide_impl.hpp"
+#include "fold_impl.hpp"
 
 namespace bl {
 
@@ -10,9 +11,22 @@ hipError_t wide_potrf_f32_lower(int n, float* a, int64_t lda, int64_t stride, in
                                 int32_t* info, hipStream_t s);
 hipError_t wide_potrf_f32_upper(int n, float* a, int64_t lda, int64_t stride, int64_t batch,
                                 int32_t* info, hipStream_t s);
+hipError_t fold_potrf_f32(bool upper, int n, float* a, int64_t lda, int64_t stride, int64_t batch,
+                          int32_t* info, hipStream_t s);
 
 namespace {
 bool wide_order(int n) { return n > tiny_detail::last_nb(tiny_detail::TinyConfigs<float>::type{}); }
+// The folded window where it measured faster on MI355X (b16384, against the
+// window it replaces): Lower 34..64 (1.06-1.23x the 64 x 1 window; Upper there
+// 0.93-0.95x), Upper 97..128 (1.27-1.62x the rows layout, whose Upper loads
+// are per row; Lower there 0.55-0.60x, the rows layout already skipping the
+// triangle per wavefront), and only where its wavefront's matrices fit the
+// 31-bit offsets.
+bool use_fold(bool upper, int n, int64_t stride) {
+    if (!upper && n >= 34 && n <= 64) return fold_detail::fold_layout_ok<float, 64>(stride);
+    if (upper && n >= 97 && n <= 128) return fold_detail::fold_layout_ok<float, 128>(stride);
+    return false;
+}
 }  // namespace
 
 int tiny_max_n_f32() { return wide_detail::kWideMaxOrder; }
@@ -23,6 +37,11 @@ bool tiny_layout_ok_f32(int n, int64_t stride) {
 }
 
 bool tiny_geometry_f32(bool upper, int n, int64_t lda, int64_t stride, int64_t batch, Geometry& g) {
+    if (use_fold(upper, n, stride)) {
+        if (n <= 64) fold_detail::fold_geometry<float, 64>(upper, batch, g);
+        else fold_detail::fold_geometry<float, 128>(upper, batch, g);
+        return true;
+    }
     if (wide_order(n)) {
         if (n > wide_detail::kWideMaxOrder) return false;
         wide_detail::wide_geometry<float>(n, batch, g);
@@ -33,6 +52,7 @@ bool tiny_geometry_f32(bool upper, int n, int64_t lda, int64_t stride, int64_t b
 
 hipError_t tiny_potrf_f32(bool upper, int n, void* A, int64_t lda, int64_t stride, int64_t batch,
                           int32_t* info, hipStream_t s) {
+    if (use_fold(upper, n, stride)) return fold_potrf_f32(upper, n, static_cast<float*>(A), lda, stride, batch, info, s);
     if (wide_order(n)) {
         if (n > wide_detail::kWideMaxOrder) return hipErrorInvalidValue;
         float* a = static_cast<float*>(A);

@@ -21,7 +21,7 @@ bool wide_order(int n) { return n > tiny_detail::last_nb(tiny_detail::TinyConfig
 // orders 33..64 in the folded window where a pair of matrices fits its 31-bit
 // offsets (else the one-wavefront window)
 bool use_fold(int n, int64_t stride) {
-    return n >= fold_detail::kFoldMin && n <= fold_detail::kFoldMax && fold_detail::fold_layout_ok<double>(stride);
+    return n >= fold_detail::kFoldMin && n <= fold_detail::kFoldMax && fold_detail::fold_layout_ok<double, 64>(stride);
 }
 }  // namespace
 
@@ -40,7 +40,7 @@ bool tiny_geometry_f64(bool upper, int n, int64_t lda, int64_t stride, int64_t b
         return true;
     }
     if (use_fold(n, stride)) {
-        fold_detail::fold_geometry<double>(upper, batch, g);
+        fold_detail::fold_geometry<double, 64>(upper, batch, g);
         return true;
     }
     return tiny_detail::geometry_t<double>(upper, n, lda, stride, batch, g);

@@ -225,6 +225,8 @@ def test_route_wide_window_geometry(lib):
     assert (tile_waves(129), tile_waves(160), tile_waves(192)) == (11, 11, 12)
     for uplo in ("L", "U"):
         for n in (65, 96, 97, 128, 129, 160, 192):
+            if uplo == "U" and 97 <= n <= 128:
+                continue                  # the folded window (below)
             threads = 128 if n <= 128 else 64 * tile_waves(n)
             for batch in (1, 1000, (1 << 20) + 5):
                 r = bl.route("f32", uplo, n, batch, family="tiny")
@@ -280,8 +282,24 @@ def test_route_folded_window_geometry(lib):
     # the neighbours: order 32 in a smaller register window, 65 in the wide window
     assert bl.route("f64", "L", 32, 1000)["matrices_per_wave"] > 2
     assert bl.route("f64", "L", 65, 1000)["block_threads"] > 64
+    # fp32: the folded window for Lower at 34..64 (Upper keeps 64 x 1; order 33
+    # has its own window) and for Upper at 97..128, one matrix per wavefront
+    # (Lower keeps the rows layout)
     for n in (34, 48, 64):
-        assert bl.route("f32", "L", n, 1000)["lanes_per_matrix"] == 64
+        r = bl.route("f32", "L", n, 1001)
+        assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == (32, 2, 2)
+        assert r["grid"] == 501 and r["lds_bytes"] == 2 * 2 * 68 * 4
+        assert bl.route("f32", "U", n, 1000)["lanes_per_matrix"] == 64
+    assert bl.route("f32", "L", 33, 1000)["lanes_per_matrix"] == 11
+    for n in (97, 112, 128):
+        for batch in (1, 1000, (1 << 20) + 5):
+            r = bl.route("f32", "U", n, batch)
+            assert r["family"] == "tiny" and r["block_threads"] == 64
+            assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == (64, 2, 1)
+            assert r["grid"] == min(batch, 1 << 19)
+            assert r["lds_bytes"] == (2 * 132 + 128 * 33) * 4
+        assert bl.route("f32", "L", n, 1000)["block_threads"] == 128
+    assert bl.route("f32", "U", 96, 1000)["block_threads"] == 128
 
 
 def test_tiny_grid_is_capped_for_huge_batches(lib):

@@ -1,14 +1,16 @@
-"""GPU parity of the tiny family's folded window against the CPU oracle: fp64
-and cfloat at orders 33..64, two matrices per wavefront, lane q holding rows q
-and 63 - q of its matrix (rows at or beyond n hold the identity); Upper moves
-the matrix through LDS in slabs of whole cache lines.
+"""GPU parity of the tiny family's folded window against the CPU oracle: a
+window of NB rows on NB / 2 lanes per matrix, lane q holding rows q and
+NB - 1 - q (rows at or beyond n hold the identity); Upper moves the matrix
+through LDS in slabs of whole cache lines.  NB = 64 (two matrices per
+wavefront) serves fp64 and cfloat at orders 33..64 and fp32 Lower at 34..64;
+NB = 128 (one matrix per wavefront) serves fp32 Upper at 97..128.
 
 Same bar as the other families: info bit-exact on every item, the referenced
 triangle within 1e-4 (cfloat) or 1e-11 (fp64) relative Frobenius error per
 item, the other triangle and the padding untouched.  The cases aim at what is
-particular to the window: failures on either side of the fold (rows 31 and 32
-are the short and the long row of lane 31), Schur pivots that only fail after
-updates across it, a second matrix of the pair that does not exist (odd
+particular to the window: failures on either side of the fold (rows NB/2 - 1
+and NB/2 are the short and the long row of the last lane), Schur pivots that
+only fail after updates across it, a second matrix of the pair that does not exist (odd
 batches, batch 1), batches beyond the launch's grid cap, strides whose pair of
 matrices overflows the 31-bit offsets (then the one-wavefront window serves),
 and thousands of distinct items.  Every order and the padded layouts are in
@@ -26,6 +28,9 @@ pytestmark = pytest.mark.gpu
 
 UPLOS = ["L", "U"]
 DTS = ["f64", "c64"]
+# (dtype, triangle, orders) served by the folded window
+ROUTES = [(dt, uplo, (33, 48, 64)) for dt in DTS for uplo in UPLOS] + \
+         [("f32", "L", (34, 48, 64)), ("f32", "U", (97, 112, 128))]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -43,43 +48,47 @@ def _bits(t):
     return t.view(torch.int64)
 
 
-@pytest.mark.parametrize("dt", DTS)
-@pytest.mark.parametrize("uplo", UPLOS)
-@pytest.mark.parametrize("n", [33, 48, 64])
+def _route_cases():
+    return [(dt, uplo, n) for dt, uplo, orders in ROUTES for n in orders]
+
+
+@pytest.mark.parametrize("dt,uplo,n", _route_cases())
 def test_fold_info_first_failure_nan_and_stale_pivot(dt, uplo, n):
     """The first failing column wins; NaN and zero pivots fail; a pivot that
     goes non-positive only in its Schur complement fails at that column, here
-    with the chain crossing the fold (rows 30, 31 short, row 32 long)."""
+    with the chain crossing the fold (rows h - 2, h - 1 short, row h long, for
+    h = NB/2)."""
     import dense_linear_algebra_potrf_amd as bl
+    h = 32 if n <= 64 else 64
     r = bl.route(dt, uplo, n, 9, family="tiny")
-    assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == (32, 2, 2)
+    assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == (h, 2, 64 // h)
     a = syn.spd_matrices(n, 9, dt, seed=71 + n)
     a[0, 3, 3] *= -1
     a[0, n - 2, n - 2] *= -1                  # two plants: the first wins
     a[1, 0, 0] = syn.nan_value(dt)            # NaN pivot in the first column
-    a[2, 32, 32] = syn.nan_value(dt)          # the first long row's own pivot
+    a[2, h, h] = syn.nan_value(dt)            # the first long row's own pivot
     a[3, n - 1, n - 1] = -a[3, n - 1, n - 1]  # last column
     stale = np.eye(n)
-    idx = [30, 31, 32]
+    idx = [h - 2, h - 1, h]
     stale[np.ix_(idx, idx)] = [[1, .75, .75], [.75, 1, -.75], [.75, -.75, 1]]
-    a[4] = stale.astype(a.dtype)              # unit diagonal: only the Schur pivot of column 33 fails
-    a[5, 31, 31] = 0                          # exact zero pivot on the last short row
+    a[4] = stale.astype(a.dtype)              # unit diagonal: only the Schur pivot of column h + 1 fails
+    a[5, h - 1, h - 1] = 0                    # exact zero pivot on the last short row
     a[6, 16, 16] *= -1
     stale2 = np.eye(n)
     idx2 = [n - 3, n - 2, n - 1]
     stale2[np.ix_(idx2, idx2)] = [[1, .75, .75], [.75, 1, -.75], [.75, -.75, 1]]
     a[7] = stale2.astype(a.dtype)             # the chain at the last rows (long rows only)
     _, _, info = check_potrf(a, uplo, family="tiny", label="fold-info")
-    assert list(info) == [4, 1, 33, n, 33, 32, 17, n, 0]
+    assert list(info) == [4, 1, h + 1, n, h + 1, h, 17, n, 0]
 
 
-@pytest.mark.parametrize("dt", DTS)
-@pytest.mark.parametrize("uplo", UPLOS)
-def test_fold_small_and_odd_batches(dt, uplo):
-    """Batches of 1, 2, 3 and 129: the last pair's second matrix is missing
-    whenever the batch is odd; nothing of it is read or written (the padded
-    layout keeps sentinels around every matrix)."""
-    for n in (33, 47, 64):
+@pytest.mark.parametrize("dt,uplo,orders", ROUTES)
+def test_fold_small_and_odd_batches(dt, uplo, orders):
+    """Batches of 1, 2, 3 and 129: with two matrices per wavefront the last
+    one's second matrix is missing whenever the batch is odd; nothing of it is
+    read or written (the padded layout keeps sentinels around every matrix)."""
+    lo, hi = orders[0], orders[-1]
+    for n in (lo, (lo + hi) // 2 | 1, hi):
         for batch in (1, 2, 3, 129):
             a = syn.spd_matrices(n, batch, dt, seed=n * 7 + batch)
             want = syn.plant_failures(a, seed=batch, every=3)
@@ -89,16 +98,17 @@ def test_fold_small_and_odd_batches(dt, uplo):
 
 
 @pytest.mark.parametrize("dt,uplo,n", [("c64", "U", 33), ("c64", "L", 48), ("f64", "L", 33),
-                                       ("f64", "U", 40)])
+                                       ("f64", "U", 40), ("f32", "L", 40), ("f32", "U", 100)])
 def test_fold_batch_beyond_the_grid_cap_is_uniform(dt, uplo, n):
-    """More pairs than the launch's workgroups (2^19): every workgroup loops
-    over several pairs, and the odd batch leaves the last pair half empty.
-    Identical items give the solo result bit for bit; compared on the device."""
+    """More wavefronts of matrices than the launch's workgroups (2^19): every
+    workgroup loops over several, and with two matrices per wavefront the odd
+    batch leaves the last one half empty.  Identical items give the solo
+    result bit for bit; compared on the device."""
     import torch
     import dense_linear_algebra_potrf_amd as bl
     batch = (1 << 20) + 5
     r = bl.route(dt, uplo, n, batch, family="tiny")
-    assert r["grid"] == 1 << 19 and r["matrices_per_wave"] == 2
+    assert r["grid"] == 1 << 19 and r["grid"] * r["matrices_per_wave"] < batch
     one = syn.spd_matrices(n, 1, dt, seed=3 * n)
     solo = torch.from_numpy(syn.to_colmajor(one)).cuda()
     bl.potrf(solo, uplo, n=n, batch=1, family="tiny")
@@ -112,7 +122,7 @@ def test_fold_batch_beyond_the_grid_cap_is_uniform(dt, uplo, n):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("dt,uplo", [("c64", "L"), ("f64", "U")])
+@pytest.mark.parametrize("dt,uplo", [("c64", "L"), ("f64", "U"), ("f32", "L")])
 def test_fold_stride_beyond_a_pair_uses_the_one_wavefront_window(dt, uplo):
     """A stride whose pair of matrices overflows the 31-bit buffer offsets
     while one matrix fits: the route keeps the tiny family's one-wavefront
@@ -122,15 +132,16 @@ def test_fold_stride_beyond_a_pair_uses_the_one_wavefront_window(dt, uplo):
     import oracle
     from tests._checks import TOL, rel_err_triangle
     n, batch = 40, 2
-    stride = (1 << 31) // 16 + 64                  # 2 stride elements > 2^31 bytes > stride elements
+    es = 4 if dt == "f32" else 8
+    stride = (1 << 31) // (2 * es) + 64            # 2 stride elements > 2^31 bytes > stride elements
     r = bl.route(dt, uplo, n, batch, stride=stride)
     assert r["family"] == "tiny" and r["lanes_per_matrix"] == 64, r
     a = syn.spd_matrices(n, batch, dt, seed=17)
     syn.plant_failures(a, seed=5, every=2)
     dense = syn.to_colmajor(a)
     announce("fold stride fallback", dt, uplo, f"n={n}", f"stride={stride}")
-    t = torch.zeros(stride * (batch - 1) + n * n, dtype=torch.float64 if dt == "f64" else torch.complex64,
-                    device="cuda")
+    tdt = {"f32": torch.float32, "f64": torch.float64, "c64": torch.complex64}[dt]
+    t = torch.zeros(stride * (batch - 1) + n * n, dtype=tdt, device="cuda")
     for b in range(batch):
         t[b * stride:b * stride + n * n] = torch.from_numpy(dense[b * n * n:(b + 1) * n * n]).cuda()
     info = bl.potrf(t, uplo, n=n, batch=batch, stride=stride)
@@ -148,7 +159,8 @@ def test_fold_stride_beyond_a_pair_uses_the_one_wavefront_window(dt, uplo):
 
 
 @pytest.mark.parametrize("dt,uplo,n,batch", [("c64", "U", 64, 4096), ("c64", "L", 40, 2049),
-                                              ("f64", "L", 48, 4096), ("f64", "U", 64, 2047)])
+                                              ("f64", "L", 48, 4096), ("f64", "U", 64, 2047),
+                                              ("f32", "L", 64, 4095), ("f32", "U", 128, 2048)])
 def test_fold_batch_of_distinct_items_matches_the_oracle_at_every_item(dt, uplo, n, batch):
     """Thousands of distinct matrices (cfloat Upper n = 64: the secondary
     workload's shape): every item against the oracle, in chunks."""
