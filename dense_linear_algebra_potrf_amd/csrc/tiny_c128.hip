@@ -25,7 +25,7 @@ bool tiny_layout_ok_c128(int n, int64_t stride) {
 bool tiny_geometry_c128(bool upper, int n, int64_t lda, int64_t stride, int64_t batch, Geometry& g) {
     if (wide_order(n)) {
         if (n > wide_detail::kWideMaxOrder) return false;
-        wide_detail::wide_geometry<cdouble>(n, batch, g);
+        wide_detail::wide_geometry<cdouble>(upper, n, batch, g);
         return true;
     }
     return tiny_detail::geometry_t<cdouble>(upper, n, lda, stride, batch, g);

@@ -36,7 +36,7 @@ bool tiny_layout_ok_c64(int n, int64_t stride) {
 bool tiny_geometry_c64(bool upper, int n, int64_t lda, int64_t stride, int64_t batch, Geometry& g) {
     if (wide_order(n)) {
         if (n > wide_detail::kWideMaxOrder) return false;
-        wide_detail::wide_geometry<cfloat>(n, batch, g);
+        wide_detail::wide_geometry<cfloat>(upper, n, batch, g);
         return true;
     }
     if (use_fold(n, stride)) {

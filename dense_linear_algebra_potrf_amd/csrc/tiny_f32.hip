@@ -44,7 +44,7 @@ bool tiny_geometry_f32(bool upper, int n, int64_t lda, int64_t stride, int64_t b
     }
     if (wide_order(n)) {
         if (n > wide_detail::kWideMaxOrder) return false;
-        wide_detail::wide_geometry<float>(n, batch, g);
+        wide_detail::wide_geometry<float>(upper, n, batch, g);
         return true;
     }
     return tiny_detail::geometry_t<float>(upper, n, lda, stride, batch, g);

@@ -35,7 +35,8 @@
 //
 // Loads and stores (Lower): lanes of a wavefront hold consecutive rows, so
 // each column is one coalesced access of 64 consecutive elements.  Upper reads
-// S(i, c) = A(c, i), a row of A per lane.
+// S(i, c) = A(c, i): the tiles layout a row of A per lane, the rows layout in
+// slabs of whole column lines through an LDS tile.
 #pragma once
 
 #include "families.hpp"
@@ -143,10 +144,22 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void p
     int32_t* __restrict__ info)
 {
     __shared__ __attribute__((aligned(16))) float colbuf[2][kWideSlots];
+    // Upper: lane i's row is column i of A, so loads and stores per row would
+    // touch a cache line per lane and element.  The referenced triangle moves
+    // instead in slabs of 32 rows of A (one 128-byte line of every column):
+    // each instruction of the workgroup covers four whole column lines, and a
+    // tile of 32 elements (plus one of padding) for each of the workgroup's
+    // 128 rows transposes the slab (rows beyond NC are idle: they read what
+    // the tile holds and write their own slots, which no one reads).  Each
+    // final column of the factor goes into the tile at its step; every 32
+    // steps the slab is written out as whole lines.
+    constexpr int SR = 32, PITCH = SR + 1;
+    __shared__ __attribute__((aligned(16))) float tile[UPPER ? 128 * PITCH : 1];
     const int lane = threadIdx.x & 63;
     const int q16 = lane & 15;                // lane within its row of 16 (DPP broadcasts)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = wave * 64 + lane;           // this lane's row
+    const int lr = threadIdx.x & 31, lc = threadIdx.x >> 5;   // slab: row of A, column within 4
 
     // the whole matrix for the wavefront whose rows end at KE
     auto run = [&](auto kec, int64_t b) __attribute__((always_inline)) {
@@ -156,12 +169,45 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void p
         // only reads the column entries of rows at or above it, so their values
         // never reach a row below n.  Their first zero pivot (step n) only marks
         // info n + 1, which is cleared at the end.
+        // Upper, slabs: element (row r, column c) of A, out of range unless
+        // r <= c < n (row and column behind opaque copies at every use)
+        auto slab_off = [&](int c, int r) __attribute__((always_inline)) {
+            c = opaque_row(c);
+            r = opaque_row(r);
+            return (r <= c && c < n) ? uint32_t(c) * m.lda_b + uint32_t(r) * 4u : kBufOOB;
+        };
         float a[KE];
-        const int il = opaque_row(i);
-        static_for<0, KE>([&](auto cc) {
-            constexpr int c = cc;
-            a[c] = buf_load<float>(m.rs, m.off<UPPER>(il, c, n), m.col_off<UPPER>(c));
-        });
+        if constexpr (!UPPER) {
+            const int il = opaque_row(i);
+            static_for<0, KE>([&](auto cc) {
+                constexpr int c = cc;
+                a[c] = buf_load<float>(m.rs, m.off<UPPER>(il, c, n), m.col_off<UPPER>(c));
+            });
+        } else {
+            // slab sb: rows 32 sb .. 32 sb + 31 of A in the columns that reach
+            // them (>= 32 sb); entries right of a row's diagonal are left as
+            // they come (never stored, never read by a referenced entry)
+            static_for<0, NC / SR>([&](auto sbc) {
+                constexpr int sb = sbc, U0 = sb * SR / 4, NU = NC / 4;
+                float st[NU - U0];
+                static_for<U0, NU>([&](auto uc) {
+                    constexpr int u = uc;
+                    st[u - U0] = buf_load<float>(m.rs, slab_off(u * 4 + lc, sb * SR + lr));
+                });
+                float* tw = tile + opaque_row(lc * PITCH + lr);
+                static_for<U0, NU>([&](auto uc) {
+                    constexpr int u = uc;
+                    tw[u * 4 * PITCH] = st[u - U0];
+                });
+                __syncthreads();
+                const float* tr = tile + opaque_row(i * PITCH);
+                static_for<0, SR>([&](auto rc) {
+                    constexpr int c = sb * SR + rc;
+                    if constexpr (c < KE) a[c] = tr[rc];
+                });
+                __syncthreads();
+            });
+        }
         int32_t inf = 0;
         colbuf[0][i] = a[0];
         __syncthreads();
@@ -180,13 +226,25 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void p
                     colbuf[(j + 1) & 1][i] = a[j + 1];
                 }
                 wide_update<j + 2, KE>(a, col, 0, q16, WideMult<float>{-t});
-                // column j is final: to the matrix now (one coalesced column),
-                // which frees its register for the rest of the factorisation
+                // column j is final: to the matrix now (Lower: one coalesced
+                // column; Upper: into the tile), which frees its register for
+                // the rest of the factorisation
                 const int is = opaque_row(i);
                 const float lij = (is == j) ? sq : a[j] * rsd;
-                buf_store<float>(m.rs, m.off<UPPER>(is, j, n), lij, m.col_off<UPPER>(j));
+                if constexpr (UPPER) tile[is * PITCH + j % SR] = lij;
+                else buf_store<float>(m.rs, m.off<UPPER>(is, j, n), lij, m.col_off<UPPER>(j));
             }
             __syncthreads();
+            if constexpr (UPPER && j % SR == SR - 1) {
+                // slab j / 32 of the factor, as whole lines of A (every thread)
+                constexpr int sb = j / SR, U0 = sb * SR / 4, NU = NC / 4;
+                const float* tr = tile + opaque_row(lc * PITCH + lr);
+                static_for<U0, NU>([&](auto uc) {
+                    constexpr int u = uc;
+                    buf_store<float>(m.rs, slab_off(u * 4 + lc, sb * SR + lr), tr[u * 4 * PITCH]);
+                });
+                __syncthreads();
+            }
         });
         // the second wavefront reads every pivot (the first stops at its last row)
         if (wave == 1 && lane == 0 && info != nullptr) info[b] = inf > n ? 0 : inf;
@@ -313,7 +371,7 @@ template <typename T>
 inline int wide_threads(int n) { return wide_rows<T>(n) ? 128 : 64 * wide_tile_waves(n); }
 
 template <typename T>
-inline void wide_geometry(int n, int64_t batch, Geometry& g) {
+inline void wide_geometry(bool upper, int n, int64_t batch, Geometry& g) {
     g.family = FAM_TINY;
     g.threads = wide_threads<T>(n);
     g.P = g.threads;                                         // lanes sharing one matrix
@@ -322,6 +380,7 @@ inline void wide_geometry(int n, int64_t batch, Geometry& g) {
     g.panel = wide_rows<T>(n) ? 0 : kTileCols;               // columns of a tile
     g.grid = batch < kWideMaxGrid ? batch : kWideMaxGrid;
     g.lds = int64_t(2) * kWideSlots * int64_t(sizeof(T));
+    if (upper && wide_rows<T>(n)) g.lds += int64_t(128) * 33 * 4;   // the slab tile
 }
 
 // Enqueue one element type and triangle (instantiated by its translation unit).
