@@ -33,13 +33,30 @@ namespace fold_detail {
 constexpr int kFoldMin = 33, kFoldMax = 64;
 constexpr int64_t kFoldMaxGrid = int64_t(1) << 19;     // workgroups of one wavefront
 
-template <int NB> constexpr int fold_half() { return NB / 2; }          // lanes per matrix
-template <int NB> constexpr int fold_mpw() { return 64 / (NB / 2); }    // matrices per wavefront
+template <int NB> constexpr int fold_half() { return NB / 2; }          // lanes holding rows of a matrix
+// lanes per matrix group: NB / 2, except that the 48-row window takes groups
+// of 32 lanes (8 idle), so that a DPP row of 16 lanes never spans two matrices
+template <int NB> constexpr int fold_gsize() { return NB == 48 ? 32 : NB / 2; }
+template <int NB> constexpr int fold_mpw() { return 64 / fold_gsize<NB>(); }    // matrices per wavefront
+// lane groups in a wavefront, an idle tail included (each has its pivot
+// buffers, so idle lanes need no guard)
+template <int NB> constexpr int fold_groups() { return (64 + fold_gsize<NB>() - 1) / fold_gsize<NB>(); }
+// slots of a pivot buffer: the NB rows, two spare slots per idle lane of a
+// group, padding
+template <int NB> constexpr int fold_slot() { return NB + 2 * (fold_gsize<NB>() - NB / 2) + 4; }
 template <typename T> constexpr int fold_slab_rows() { return 128 / int(sizeof(T)); }
+// occupancy asked of the compiler, from the registers a lane's values take:
+// the 34-row window (51 fp32 values) six wavefronts per SIMD, up to 72
+// registers four, more two (144 registers of values at three wavefronts
+// spilled)
+template <typename T, int NB>
+constexpr int fold_waves_per_eu() {
+    return NB <= 34 ? 6 : (3 * NB / 2) * int(sizeof(T)) / 4 <= 72 ? 4 : 2;
+}
 // LDS elements: the pivot buffers, and for Upper the slab tile
 template <typename T, int NB, bool UPPER>
 constexpr int fold_lds_elems() {
-    return 2 * fold_mpw<NB>() * (NB + 4) + (UPPER ? fold_mpw<NB>() * NB * (fold_slab_rows<T>() + 1) : 0);
+    return 2 * fold_groups<NB>() * fold_slot<NB>() + (UPPER ? fold_mpw<NB>() * NB * (fold_slab_rows<T>() + 1) : 0);
 }
 
 // An opaque copy: the column and row indices of the slab passes are shared by
@@ -51,12 +68,12 @@ __device__ __forceinline__ int opaque_v(int v) {
 }
 
 template <typename T, int NB, bool UPPER>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void potrf_fold_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(fold_waves_per_eu<T, NB>()))) void potrf_fold_kernel(
     T* __restrict__ A, int n, int64_t lda, int64_t stride, int64_t batch, int32_t* __restrict__ info)
 {
     using R = typename Traits<T>::R;
     constexpr uint32_t S = sizeof(T);
-    constexpr int HALF = fold_half<NB>(), MPW = fold_mpw<NB>();
+    constexpr int HALF = fold_half<NB>(), GS = fold_gsize<NB>(), MPW = fold_mpw<NB>();
     // Upper: lane q's rows are columns of A, so loads and stores per row would
     // touch a cache line per lane and element.  The referenced triangle
     // instead moves in slabs of SR rows of A (SR elements = one 128-byte line
@@ -65,22 +82,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void po
     // (a column's SR elements plus one element of padding), and every lane
     // picks its two columns out of it.  A slab of the factor is written as
     // soon as its SR columns are final.
-    constexpr int SR = fold_slab_rows<T>(), LPI = HALF / SR, PITCH = SR + 1;
-    constexpr int SLOT = NB + 4, CB = 2 * MPW * SLOT;
-    static_assert(HALF % 16 == 0 && 64 % HALF == 0 && LPI >= 1 && HALF % SR == 0, "fold geometry");
+    constexpr int SR = fold_slab_rows<T>(), LPI = HALF / SR > 0 ? HALF / SR : 1, PITCH = SR + 1;
+    constexpr int GROUPS = fold_groups<NB>(), SLOT = fold_slot<NB>(), CB = 2 * GROUPS * SLOT;
+    // DPP broadcasts need rows of 16 lanes within one matrix
+    constexpr bool DPP = !Traits<T>::cplx && GS % 16 == 0 && NB % 16 == 0;
+    static_assert(NB % 2 == 0 && HALF <= GS && GS <= 64, "fold geometry");
+    static_assert(!UPPER || (GS == HALF && 64 % HALF == 0 && HALF % SR == 0), "Upper slab geometry");
     static_assert((HALF + NB) * int(S) <= 192 * 4, "two rows per lane in 192 registers");
     __shared__ __attribute__((aligned(16))) T lds[fold_lds_elems<T, NB, UPPER>()];
-    auto colbuf = [&](int par, int mh) __attribute__((always_inline)) { return lds + (par * MPW + mh) * SLOT; };
+    auto colbuf = [&](int par, int mh) __attribute__((always_inline)) { return lds + (par * GROUPS + mh) * SLOT; };
 
     const int lane = threadIdx.x & 63;
-    const int h = lane / HALF;                // which matrix of the wavefront
-    const int q = lane % HALF;
+    const int h = lane / GS;                  // which matrix of the wavefront
+    const int q = lane % GS;
+    const bool own = q < HALF;                // (the 48-row window's lanes 24..31 of a group are idle)
     const int q16 = lane & 15;                // lane within its row of 16 (DPP broadcasts)
     const uint32_t lda_b = uint32_t(lda) * S;
 
     for (int64_t m0 = MPW * int64_t(blockIdx.x); m0 < batch; m0 += MPW * int64_t(gridDim.x)) {
         const int64_t mat = m0 + h;
-        const bool live = mat < batch;
+        const bool live = h < MPW && mat < batch;    // (lanes past MPW groups are idle)
         // one descriptor for the wavefront's matrices (a descriptor must be the
         // same for the whole wavefront), matrix h at a byte offset inside it
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(A + m0 * stride);
@@ -92,7 +113,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void po
             asm volatile("" : "+v"(row));
             uint32_t ldb = lda_b;            // (the column offsets are formed where used)
             asm volatile("" : "+s"(ldb));
-            int lim = live ? n : 0;          // a missing matrix has no rows
+            int lim = live && (UPPER || own) ? n : 0;   // a missing matrix (or an idle lane) has no rows
             asm volatile("" : "+v"(lim));
             uint32_t mb = mbase;             // (else mbase + c S is held for every c)
             asm volatile("" : "+v"(mb));
@@ -110,6 +131,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void po
         };
         T xa[HALF], xb[NB];
         const int ra = q, rb = NB - 1 - q;
+        // pivot-buffer slots written: the two rows, or an idle lane's spares
+        const int wa = own ? ra : NB + 2 * (q - HALF), wb = own ? rb : NB + 2 * (q - HALF) + 1;
         if constexpr (!UPPER) {
             // in fenced groups of 16 loads: formed all at once, the masked
             // offsets of every load would be live beside the values they load
@@ -171,8 +194,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void po
             wave_lds_sync();
         };
         int32_t inf = 0;
-        colbuf(0, h)[ra] = xa[0];
-        colbuf(0, h)[rb] = xb[0];
+        colbuf(0, h)[wa] = xa[0];
+        colbuf(0, h)[wb] = xb[0];
         wave_lds_sync();
         static_for<0, NB>([&](auto jj) {
             constexpr int j = jj;
@@ -189,22 +212,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void po
                 const T cj1 = col[j + 1];
                 if constexpr (j + 1 < HALF) {
                     sub_mul_conj(xa[j + 1], ta, cj1);
-                    colbuf((j + 1) & 1, h)[ra] = xa[j + 1];
+                    colbuf((j + 1) & 1, h)[wa] = xa[j + 1];
                 }
                 sub_mul_conj(xb[j + 1], tb, cj1);
-                colbuf((j + 1) & 1, h)[rb] = xb[j + 1];
+                colbuf((j + 1) & 1, h)[wb] = xb[j + 1];
                 wave_lds_sync();
             }
-            // the rest.  Real types: group by group of 16 entries by DPP row
-            // broadcasts, each group's read issued one group ahead of its
-            // updates.  Complex types: every lane reads the entries, in chunks
-            // of 32 bytes, each chunk one ahead of its updates, with
-            // scheduling fences between chunks (left alone, the compiler reads
-            // the whole column ahead and spills); the four multiply-adds of a
-            // complex update measured slower as DPP broadcasts.
+            // the rest.  Real types with rows of 16 lanes in one matrix: group
+            // by group of 16 entries by DPP row broadcasts, each group's read
+            // issued one group ahead of its updates.  Otherwise every lane
+            // reads the entries, in chunks of 32 bytes, each chunk one ahead
+            // of its updates, with scheduling fences between chunks (left
+            // alone, the compiler reads the whole column ahead and spills);
+            // the four multiply-adds of a complex update measured slower as
+            // DPP broadcasts.
             constexpr int K0 = j + 2;
-            if constexpr (Traits<T>::cplx && K0 < NB) {
-                constexpr int CH = 32 / int(S);
+            if constexpr (!DPP && K0 < NB) {
+                constexpr int CH = (NB <= 34 ? 16 : 32) / int(S);   // (16 bytes: the 34-row window at six wavefronts per SIMD)
                 constexpr int NCH = (NB - K0 + CH - 1) / CH;
                 T cv[2][CH];
                 auto fetch_chunk = [&](auto cc) __attribute__((always_inline)) {

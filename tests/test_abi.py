@@ -266,18 +266,20 @@ def test_route_folded_window_geometry(lib):
     one-wavefront window; fp32 keeps that window at these orders."""
     for dt, es in (("f64", 8), ("c64", 8)):
         for uplo in ("L", "U"):
-            for n in (33, 40, 63, 64):
+            for n in (33, 40, 48, 49, 63, 64):
                 for batch in (1, 2, 1001, (1 << 20) + 5):
                     r = bl.route(dt, uplo, n, batch)
                     assert r["family"] == "tiny", (dt, n)
+                    # Lower up to 48: the 48-row window (24 lanes of a 32-lane group)
+                    half = 24 if uplo == "L" and n <= 48 else 32
                     assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == \
-                        (32, 2, 2)
+                        (half, 2, 2)
                     assert r["block_threads"] == 64
                     assert r["grid"] == min((batch + 1) // 2, 1 << 19)
                     lds = 2 * 2 * 68 * es + (2 * 64 * (128 // es + 1) * es if uplo == "U" else 0)
                     assert r["lds_bytes"] == lds
         top = (1 << 31) // es // 2                  # largest stride whose pair fits, with margin
-        assert bl.route(dt, "L", 40, 4, stride=top - 1)["lanes_per_matrix"] == 32
+        assert bl.route(dt, "L", 40, 4, stride=top - 1)["lanes_per_matrix"] == 24
         r = bl.route(dt, "L", 40, 4, stride=top + 64)
         assert r["family"] == "tiny" and r["lanes_per_matrix"] == 64 and r["matrices_per_wave"] == 1
     # the neighbours: order 32 in a smaller register window, 65 in the wide window
@@ -286,12 +288,17 @@ def test_route_folded_window_geometry(lib):
     # fp32: the folded window for Lower at 34..64 (Upper keeps 64 x 1; order 33
     # has its own window) and for Upper at 97..128, one matrix per wavefront
     # (Lower keeps the rows layout)
-    for n in (34, 48, 64):
+    for n in (35, 48, 49, 64):
         r = bl.route("f32", "L", n, 1001)
-        assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == (32, 2, 2)
+        assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == \
+            (24 if n <= 48 else 32, 2, 2)
         assert r["grid"] == 501 and r["lds_bytes"] == 2 * 2 * 68 * 4
         assert bl.route("f32", "U", n, 1000)["lanes_per_matrix"] == 64
-    assert bl.route("f32", "L", 33, 1000)["lanes_per_matrix"] == 11
+    r = bl.route("f32", "L", 34, 1000)    # the 34-row window: 17 lanes, three matrices per wavefront
+    assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == (17, 2, 3)
+    assert r["grid"] == 334 and r["lds_bytes"] == 2 * 4 * 38 * 4
+    for uplo in ("L", "U"):               # order 33 keeps its 11 x 3 window
+        assert bl.route("f32", uplo, 33, 1000)["lanes_per_matrix"] == 11
     for n in (97, 112, 128):
         for batch in (1, 1000, (1 << 20) + 5):
             r = bl.route("f32", "U", n, batch)
