@@ -1,13 +1,15 @@
 // Folded window of the tiny family: double, both triangles (two matrices per
-// wavefront, a short and a long row per lane; Lower up to order 48 in the
-// 48-row window).
+// wavefront, a short and a long row per lane; up to order 48 in the 48-row
+// window).
 #include "fold_impl.hpp"
 
 namespace bl {
 
 hipError_t fold_potrf_f64(bool upper, int n, double* a, int64_t lda, int64_t stride, int64_t batch,
                           int32_t* info, hipStream_t s) {
-    if (!upper && n <= 48) return fold_detail::fold_launch<double, 48, false>(n, a, lda, stride, batch, info, s);
+    if (n <= 48)
+        return upper ? fold_detail::fold_launch<double, 48, true>(n, a, lda, stride, batch, info, s)
+                     : fold_detail::fold_launch<double, 48, false>(n, a, lda, stride, batch, info, s);
     return upper ? fold_detail::fold_launch<double, 64, true>(n, a, lda, stride, batch, info, s)
                  : fold_detail::fold_launch<double, 64, false>(n, a, lda, stride, batch, info, s);
 }

@@ -53,10 +53,14 @@ template <typename T, int NB>
 constexpr int fold_waves_per_eu() {
     return NB <= 34 ? 6 : (3 * NB / 2) * int(sizeof(T)) / 4 <= 72 ? 4 : 2;
 }
+// rows of a matrix's slab tile (Upper): the NB rows and two spare rows per
+// idle lane of a group
+template <int NB> constexpr int fold_tile_rows() { return NB + 2 * (fold_gsize<NB>() - NB / 2); }
 // LDS elements: the pivot buffers, and for Upper the slab tile
 template <typename T, int NB, bool UPPER>
 constexpr int fold_lds_elems() {
-    return 2 * fold_groups<NB>() * fold_slot<NB>() + (UPPER ? fold_mpw<NB>() * NB * (fold_slab_rows<T>() + 1) : 0);
+    return 2 * fold_groups<NB>() * fold_slot<NB>() +
+           (UPPER ? fold_mpw<NB>() * fold_tile_rows<NB>() * (fold_slab_rows<T>() + 1) : 0);
 }
 
 // An opaque copy: the column and row indices of the slab passes are shared by
@@ -82,12 +86,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(fold_waves_p
     // (a column's SR elements plus one element of padding), and every lane
     // picks its two columns out of it.  A slab of the factor is written as
     // soon as its SR columns are final.
-    constexpr int SR = fold_slab_rows<T>(), LPI = HALF / SR > 0 ? HALF / SR : 1, PITCH = SR + 1;
+    constexpr int SR = fold_slab_rows<T>(), LPI = GS / SR > 0 ? GS / SR : 1, PITCH = SR + 1;
+    constexpr int TR = fold_tile_rows<NB>();
     constexpr int GROUPS = fold_groups<NB>(), SLOT = fold_slot<NB>(), CB = 2 * GROUPS * SLOT;
     // DPP broadcasts need rows of 16 lanes within one matrix
     constexpr bool DPP = !Traits<T>::cplx && GS % 16 == 0 && NB % 16 == 0;
     static_assert(NB % 2 == 0 && HALF <= GS && GS <= 64, "fold geometry");
-    static_assert(!UPPER || (GS == HALF && 64 % HALF == 0 && HALF % SR == 0), "Upper slab geometry");
+    static_assert(!UPPER || (64 % GS == 0 && GS % SR == 0 && NB % SR == 0), "Upper slab geometry");
     static_assert((HALF + NB) * int(S) <= 192 * 4, "two rows per lane in 192 registers");
     __shared__ __attribute__((aligned(16))) T lds[fold_lds_elems<T, NB, UPPER>()];
     auto colbuf = [&](int par, int mh) __attribute__((always_inline)) { return lds + (par * GROUPS + mh) * SLOT; };
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(fold_waves_p
             // diagonal are left as they come (never stored nor used by a
             // referenced entry).
             const int lr = q % SR, lc = q / SR;
-            T* tile = lds + CB + h * NB * PITCH;
+            T* tile = lds + CB + h * TR * PITCH;
             static_for<0, NB / SR>([&](auto sbc) {
                 constexpr int sb = sbc, U0 = sb * SR / LPI, NU = NB / LPI;
                 T st[NU - U0];
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(fold_waves_p
         auto flush = [&](auto sbc) __attribute__((always_inline)) {
             constexpr int sb = sbc, U0 = sb * SR / LPI, NU = NB / LPI;
             const int lr = q % SR, lc = q / SR;
-            const T* tr = lds + CB + h * NB * PITCH + opaque_v(lc * PITCH + lr);
+            const T* tr = lds + CB + h * TR * PITCH + opaque_v(lc * PITCH + lr);
             wave_lds_sync();
             static_for<U0, NU>([&](auto uc) {
                 constexpr int u = uc;
@@ -271,16 +276,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(fold_waves_p
                 });
             }
             // column j is final: Lower stores it at once (the column's rows
-            // are contiguous), Upper puts it in the tile
-            auto fin = [&](int row, const T& v) __attribute__((always_inline)) {
+            // are contiguous), Upper puts it in the tile (row slot: the row,
+            // or an idle lane's spare)
+            auto fin = [&](int row, int slot, const T& v) __attribute__((always_inline)) {
                 int r2 = row;
                 asm volatile("" : "+v"(r2));
                 const T lij = select(r2 == j, diag_value<T>(sq, UPPER), scale(v, rsd));
-                if constexpr (UPPER) lds[CB + (h * NB + r2) * PITCH + j % SR] = conj(lij);
+                if constexpr (UPPER) lds[CB + (h * TR + slot) * PITCH + j % SR] = conj(lij);
                 else buf_store<T>(rs, off(r2, j), lij);
             };
-            if constexpr (j < HALF) fin(ra, xa[j]);
-            fin(rb, xb[j]);
+            if constexpr (j < HALF) fin(ra, wa, xa[j]);
+            fin(rb, wb, xb[j]);
             if constexpr (UPPER && j % SR == SR - 1) flush(ic<j / SR>{});
         });
         if (q == 0 && live && info != nullptr) info[mat] = inf > n ? 0 : inf;

@@ -270,8 +270,8 @@ def test_route_folded_window_geometry(lib):
                 for batch in (1, 2, 1001, (1 << 20) + 5):
                     r = bl.route(dt, uplo, n, batch)
                     assert r["family"] == "tiny", (dt, n)
-                    # Lower up to 48: the 48-row window (24 lanes of a 32-lane group)
-                    half = 24 if uplo == "L" and n <= 48 else 32
+                    # up to 48: the 48-row window (24 lanes of a 32-lane group)
+                    half = 24 if n <= 48 else 32
                     assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == \
                         (half, 2, 2)
                     assert r["block_threads"] == 64
