@@ -44,7 +44,10 @@ template <int NB> constexpr int fold_groups() { return (64 + fold_gsize<NB>() - 
 // slots of a pivot buffer: the NB rows, two spare slots per idle lane of a
 // group, padding
 template <int NB> constexpr int fold_slot() { return NB + 2 * (fold_gsize<NB>() - NB / 2) + 4; }
-template <typename T> constexpr int fold_slab_rows() { return 128 / int(sizeof(T)); }
+// rows of A in a slab: one 128-byte line of a column, or half a line where
+// whole lines do not divide the window (fp32 at 48 rows)
+template <typename T, int NB>
+constexpr int fold_slab_rows() { return NB % (128 / int(sizeof(T))) == 0 ? 128 / int(sizeof(T)) : 64 / int(sizeof(T)); }
 // occupancy asked of the compiler, from the registers a lane's values take:
 // the 34-row window (51 fp32 values) six wavefronts per SIMD, up to 72
 // registers four, more two (144 registers of values at three wavefronts
@@ -60,7 +63,7 @@ template <int NB> constexpr int fold_tile_rows() { return NB + 2 * (fold_gsize<N
 template <typename T, int NB, bool UPPER>
 constexpr int fold_lds_elems() {
     return 2 * fold_groups<NB>() * fold_slot<NB>() +
-           (UPPER ? fold_mpw<NB>() * fold_tile_rows<NB>() * (fold_slab_rows<T>() + 1) : 0);
+           (UPPER ? fold_mpw<NB>() * fold_tile_rows<NB>() * (fold_slab_rows<T, NB>() + 1) : 0);
 }
 
 // An opaque copy: the column and row indices of the slab passes are shared by
@@ -86,7 +89,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(fold_waves_p
     // (a column's SR elements plus one element of padding), and every lane
     // picks its two columns out of it.  A slab of the factor is written as
     // soon as its SR columns are final.
-    constexpr int SR = fold_slab_rows<T>(), LPI = GS / SR > 0 ? GS / SR : 1, PITCH = SR + 1;
+    constexpr int SR = fold_slab_rows<T, NB>(), LPI = GS / SR > 0 ? GS / SR : 1, PITCH = SR + 1;
     constexpr int TR = fold_tile_rows<NB>();
     constexpr int GROUPS = fold_groups<NB>(), SLOT = fold_slot<NB>(), CB = 2 * GROUPS * SLOT;
     // DPP broadcasts need rows of 16 lanes within one matrix

@@ -18,16 +18,17 @@ namespace {
 bool wide_order(int n) { return n > tiny_detail::last_nb(tiny_detail::TinyConfigs<float>::type{}); }
 // The folded window where it measured faster on MI355X (b16384, against the
 // window it replaces): Lower 34 in the 34-row window (1.6x the 64-row one;
-// order 33 keeps its 11 x 3 window, 44.5 against 51.7 us), Lower 35..48 in the
-// 48-row window (1.29-1.43x the 64-row one), Lower 49..64 in the 64-row window
-// (1.06-1.23x the 64 x 1 window; Upper at 34..64 0.93-0.95x), Upper
+// order 33 keeps its 11 x 3 window, 44.5 against 51.7 us), 35..48 in the
+// 48-row window (Lower 1.29-1.43x the 64-row one, Upper 1.52-1.76x the 64 x 1
+// window), Lower 49..64 in the 64-row window (1.06-1.23x the 64 x 1 window;
+// Upper there 0.93-0.95x), Upper
 // 97..128 in the 128-row window (1.27-1.62x the rows layout with per-row Upper
 // accesses, 1.03-1.08x with its slab tile; Lower there 0.55-0.60x, the rows
 // layout already skipping the triangle per wavefront), and only where a
 // wavefront's matrices fit the 31-bit offsets.
 bool use_fold(bool upper, int n, int64_t stride) {
     if (!upper && n == 34) return fold_detail::fold_layout_ok<float, 34>(stride);
-    if (!upper && n >= 35 && n <= 48) return fold_detail::fold_layout_ok<float, 48>(stride);
+    if (n >= 35 && n <= 48) return fold_detail::fold_layout_ok<float, 48>(stride);
     if (!upper && n >= 49 && n <= 64) return fold_detail::fold_layout_ok<float, 64>(stride);
     if (upper && n >= 97 && n <= 128) return fold_detail::fold_layout_ok<float, 128>(stride);
     return false;

@@ -293,7 +293,7 @@ def test_route_folded_window_geometry(lib):
         assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == \
             (24 if n <= 48 else 32, 2, 2)
         assert r["grid"] == 501 and r["lds_bytes"] == 2 * 2 * 68 * 4
-        assert bl.route("f32", "U", n, 1000)["lanes_per_matrix"] == 64
+        assert bl.route("f32", "U", n, 1000)["lanes_per_matrix"] == (24 if n <= 48 else 64)
     r = bl.route("f32", "L", 34, 1000)    # the 34-row window: 17 lanes, three matrices per wavefront
     assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == (17, 2, 3)
     assert r["grid"] == 334 and r["lds_bytes"] == 2 * 4 * 38 * 4

@@ -2,9 +2,9 @@
 window of NB rows on NB / 2 lanes per matrix, lane q holding rows q and
 NB - 1 - q (rows at or beyond n hold the identity); Upper moves the matrix
 through LDS in slabs of whole cache lines.  NB = 64 (two matrices per
-wavefront) serves fp64 and cfloat Upper at orders 33..64, Lower at 49..64 and
-fp32 Lower at 49..64; NB = 48 (24 lanes of a 32-lane group, two matrices per
-wavefront) fp64 and cfloat Lower at 33..48 and fp32 Lower at 35..48; NB = 128
+wavefront) serves fp64 and cfloat at orders 49..64 and fp32 Lower at 49..64;
+NB = 48 (24 lanes of a 32-lane group, two matrices per
+wavefront) fp64 and cfloat at 33..48 and fp32 at 35..48; NB = 128
 (one matrix per wavefront) fp32 Upper at 97..128; NB = 34 (17 lanes per
 matrix, three matrices per wavefront) fp32 Lower at 34.
 
@@ -33,7 +33,7 @@ UPLOS = ["L", "U"]
 DTS = ["f64", "c64"]
 # (dtype, triangle, orders) served by the folded window
 ROUTES = [(dt, uplo, (33, 48, 49, 64)) for dt in DTS for uplo in UPLOS] + \
-         [("f32", "L", (34, 35, 48, 49, 64)), ("f32", "U", (97, 112, 128))]
+         [("f32", "L", (34, 35, 48, 49, 64)), ("f32", "U", (35, 48, 97, 112, 128))]
 
 
 @pytest.fixture(scope="module", autouse=True)
