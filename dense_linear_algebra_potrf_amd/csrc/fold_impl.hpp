@@ -1,7 +1,7 @@
 // Folded window of the tiny family (implementation header): a window of NB rows
 // held by NB / 2 lanes per matrix, lane q holding rows q and NB - 1 - q:
-// NB = 64 (orders 33..64, two matrices per wavefront) and NB = 128 (orders up
-// to 128, one matrix per wavefront).
+// NB = 34 (17 lanes per matrix, three matrices per wavefront), NB = 48 (24
+// lanes of a 32-lane group, two), NB = 64 (two) and NB = 128 (one).
 //
 // Prior art: the BatchLAS perf_potrf page, section "potrf: the tiny tier" (lane
 // r owns row r, every value in registers) and section "The LPanel tier" (one
@@ -17,11 +17,13 @@
 // pivot never stale, the multiplier s_ij / d on the unscaled column, failures
 // as selects); the pivot column goes through LDS, double-buffered by step
 // parity, one buffer per matrix, with no barrier inside the wavefront.  For the
-// real types the updates take the column's entries by DPP row broadcasts: lane
-// q reads entry 16 g + (q mod 16) of group g, and each multiply-add takes entry
-// k from lane k mod 16 of its row of 16 lanes (all of one matrix), so one LDS
-// read serves 16 entries for both of the lane's rows.  Rows at or beyond n hold
-// the identity, so the steps past n see d = 1.
+// real types with rows of 16 lanes inside a matrix the updates take the
+// column's entries by DPP row broadcasts: lane q reads entry 16 g + (q mod 16)
+// of group g, and each multiply-add takes entry k from lane k mod 16 of its row
+// of 16 lanes, so one LDS read serves 16 entries for both of the lane's rows.
+// Rows at or beyond n hold the identity, so the steps past n see d = 1.  The
+// routes (which window serves which type, triangle and order) are chosen by
+// the tiny family's per-type translation units from measurements.
 #pragma once
 
 #include "families.hpp"
@@ -30,7 +32,7 @@
 namespace bl {
 namespace fold_detail {
 
-constexpr int kFoldMin = 33, kFoldMax = 64;
+constexpr int kFoldMin = 33, kFoldMax = 64;               // the fp64 and cfloat orders (fp32 routes its own)
 constexpr int64_t kFoldMaxGrid = int64_t(1) << 19;     // workgroups of one wavefront
 
 template <int NB> constexpr int fold_half() { return NB / 2; }          // lanes holding rows of a matrix
