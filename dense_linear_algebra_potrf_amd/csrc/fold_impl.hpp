@@ -36,9 +36,10 @@ constexpr int kFoldMin = 33, kFoldMax = 64;               // the fp64 and cfloat
 constexpr int64_t kFoldMaxGrid = int64_t(1) << 19;     // workgroups of one wavefront
 
 template <int NB> constexpr int fold_half() { return NB / 2; }          // lanes holding rows of a matrix
-// lanes per matrix group: NB / 2, except that the 48-row window takes groups
-// of 32 lanes (8 idle), so that a DPP row of 16 lanes never spans two matrices
-template <int NB> constexpr int fold_gsize() { return NB == 48 ? 32 : NB / 2; }
+// lanes per matrix group: NB / 2, except that the 48- and 56-row windows take
+// groups of 32 lanes (8 and 4 idle), so that a DPP row of 16 lanes never spans
+// two matrices
+template <int NB> constexpr int fold_gsize() { return NB == 48 || NB == 56 ? 32 : NB / 2; }
 template <int NB> constexpr int fold_mpw() { return 64 / fold_gsize<NB>(); }    // matrices per wavefront
 // lane groups in a wavefront, an idle tail included (each has its pivot
 // buffers, so idle lanes need no guard)
@@ -51,12 +52,13 @@ template <int NB> constexpr int fold_slot() { return NB + 2 * (fold_gsize<NB>() 
 template <typename T, int NB>
 constexpr int fold_slab_rows() { return NB % (128 / int(sizeof(T))) == 0 ? 128 / int(sizeof(T)) : 64 / int(sizeof(T)); }
 // occupancy asked of the compiler, from the registers a lane's values take:
-// the 34-row window (51 fp32 values) six wavefronts per SIMD, up to 72
-// registers four, more two (144 registers of values at three wavefronts
-// spilled)
+// up to 51 (the fp32 34-row window) six wavefronts per SIMD, up to 72 four,
+// more two (144 registers of values at three wavefronts spilled)
+template <typename T, int NB>
+constexpr int fold_value_regs() { return (3 * NB / 2) * int(sizeof(T)) / 4; }
 template <typename T, int NB>
 constexpr int fold_waves_per_eu() {
-    return NB <= 34 ? 6 : (3 * NB / 2) * int(sizeof(T)) / 4 <= 72 ? 4 : 2;
+    return fold_value_regs<T, NB>() <= 51 ? 6 : fold_value_regs<T, NB>() <= 72 ? 4 : 2;
 }
 // rows of a matrix's slab tile (Upper): the NB rows and two spare rows per
 // idle lane of a group
@@ -144,16 +146,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(fold_waves_p
         // pivot-buffer slots written: the two rows, or an idle lane's spares
         const int wa = own ? ra : NB + 2 * (q - HALF), wb = own ? rb : NB + 2 * (q - HALF) + 1;
         if constexpr (!UPPER) {
-            // in fenced groups of 16 loads: formed all at once, the masked
-            // offsets of every load would be live beside the values they load
+            // in fenced groups of 16 loads (8 for 16-byte elements): formed
+            // all at once, the masked offsets of every load would be live
+            // beside the values they load
+            constexpr int LG = S >= 16 ? 8 : 16;
             static_for<0, HALF>([&](auto cc) {
                 constexpr int c = cc;
-                if constexpr (c % 16 == 0) __builtin_amdgcn_sched_barrier(0);
+                if constexpr (c % LG == 0) __builtin_amdgcn_sched_barrier(0);
                 xa[c] = ident(ra, c, buf_load<T>(rs, off(ra, c)));
             });
             static_for<0, NB>([&](auto cc) {
                 constexpr int c = cc;
-                if constexpr (c % 16 == 0) __builtin_amdgcn_sched_barrier(0);
+                if constexpr (c % LG == 0) __builtin_amdgcn_sched_barrier(0);
                 xb[c] = ident(rb, c, buf_load<T>(rs, off(rb, c)));
             });
             __builtin_amdgcn_sched_barrier(0);
@@ -238,7 +242,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(fold_waves_p
             // DPP broadcasts.
             constexpr int K0 = j + 2;
             if constexpr (!DPP && K0 < NB) {
-                constexpr int CH = (NB <= 34 ? 16 : 32) / int(S);   // (16 bytes: the 34-row window at six wavefronts per SIMD)
+                // chunks of 32 bytes; 16 at six wavefronts per SIMD and for
+                // cdouble (one element), which keep those windows spill-free
+                constexpr int CH = (fold_waves_per_eu<T, NB>() >= 6 || S >= 16) ? 16 / int(S) : 32 / int(S);
                 constexpr int NCH = (NB - K0 + CH - 1) / CH;
                 T cv[2][CH];
                 auto fetch_chunk = [&](auto cc) __attribute__((always_inline)) {

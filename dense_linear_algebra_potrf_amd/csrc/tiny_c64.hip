@@ -20,8 +20,8 @@ namespace {
 bool wide_order(int n) { return n > tiny_detail::last_nb(tiny_detail::TinyConfigs<cfloat>::type{}); }
 // orders 33..64 in the folded window where a pair of matrices fits its 31-bit
 // offsets (else the one-wavefront window): up to 48 in the 48-row window
-// (Lower 1.23-1.50x the 64-row one on MI355X at b16384), the rest in the
-// 64-row one
+// (1.40-1.51x the 64-row one on MI355X at b16384), 49..56 in the 56-row window
+// (1.15-1.19x), the rest in the 64-row one
 bool use_fold(int n, int64_t stride) {
     return n >= fold_detail::kFoldMin && n <= fold_detail::kFoldMax && fold_detail::fold_layout_ok<cfloat, 64>(stride);
 }
@@ -43,6 +43,7 @@ bool tiny_geometry_c64(bool upper, int n, int64_t lda, int64_t stride, int64_t b
     }
     if (use_fold(n, stride)) {
         if (n <= 48) fold_detail::fold_geometry<cfloat, 48>(upper, batch, g);
+        else if (n <= 56) fold_detail::fold_geometry<cfloat, 56>(upper, batch, g);
         else fold_detail::fold_geometry<cfloat, 64>(upper, batch, g);
         return true;
     }

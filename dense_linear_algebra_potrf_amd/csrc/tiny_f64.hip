@@ -20,8 +20,9 @@ namespace {
 bool wide_order(int n) { return n > tiny_detail::last_nb(tiny_detail::TinyConfigs<double>::type{}); }
 // orders 33..64 in the folded window where a pair of matrices fits its 31-bit
 // offsets (else the one-wavefront window): up to 48 in the 48-row window
-// (Lower 1.23-1.50x the 64-row one on MI355X at b16384), the rest in the
-// 64-row one
+// (1.23-1.39x the 64-row one on MI355X at b16384), the rest in the 64-row one
+// (a 56-row window, without DPP updates since 56 rows are not whole groups of
+// 16, measured 0.91-0.95x at 49..56)
 bool use_fold(int n, int64_t stride) {
     return n >= fold_detail::kFoldMin && n <= fold_detail::kFoldMax && fold_detail::fold_layout_ok<double, 64>(stride);
 }

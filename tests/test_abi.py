@@ -266,22 +266,31 @@ def test_route_folded_window_geometry(lib):
     one-wavefront window; fp32 keeps that window at these orders."""
     for dt, es in (("f64", 8), ("c64", 8)):
         for uplo in ("L", "U"):
-            for n in (33, 40, 48, 49, 63, 64):
+            for n in (33, 40, 48, 49, 56, 57, 63, 64):
                 for batch in (1, 2, 1001, (1 << 20) + 5):
                     r = bl.route(dt, uplo, n, batch)
                     assert r["family"] == "tiny", (dt, n)
-                    # up to 48: the 48-row window (24 lanes of a 32-lane group)
-                    half = 24 if n <= 48 else 32
+                    # up to 48: the 48-row window (24 lanes of a 32-lane group);
+                    # cfloat 49..56 the 56-row window (28 lanes)
+                    half = 24 if n <= 48 else 28 if dt == "c64" and n <= 56 else 32
                     assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == \
                         (half, 2, 2)
                     assert r["block_threads"] == 64
                     assert r["grid"] == min((batch + 1) // 2, 1 << 19)
-                    lds = 2 * 2 * 68 * es + (2 * 64 * (128 // es + 1) * es if uplo == "U" else 0)
+                    sr = 128 // es if half != 28 else 64 // es      # slab rows: a line, or half
+                    lds = 2 * 2 * 68 * es + (2 * 64 * (sr + 1) * es if uplo == "U" else 0)
                     assert r["lds_bytes"] == lds
         top = (1 << 31) // es // 2                  # largest stride whose pair fits, with margin
         assert bl.route(dt, "L", 40, 4, stride=top - 1)["lanes_per_matrix"] == 24
         r = bl.route(dt, "L", 40, 4, stride=top + 64)
         assert r["family"] == "tiny" and r["lanes_per_matrix"] == 64 and r["matrices_per_wave"] == 1
+    # cdouble Lower 17..32: the 32-row window (16 lanes, four matrices per
+    # wavefront); Upper keeps 32 x 1
+    for n in (17, 24, 32):
+        r = bl.route("c128", "L", n, 1001)
+        assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == (16, 2, 4)
+        assert r["grid"] == 251 and r["lds_bytes"] == 2 * 4 * 36 * 16
+        assert bl.route("c128", "U", n, 1001)["lanes_per_matrix"] == 32
     # the neighbours: order 32 in a smaller register window, 65 in the wide window
     assert bl.route("f64", "L", 32, 1000)["matrices_per_wave"] > 2
     assert bl.route("f64", "L", 65, 1000)["block_threads"] > 64

@@ -1,12 +1,14 @@
 """GPU parity of the tiny family's folded window against the CPU oracle: a
 window of NB rows on NB / 2 lanes per matrix, lane q holding rows q and
 NB - 1 - q (rows at or beyond n hold the identity); Upper moves the matrix
-through LDS in slabs of whole cache lines.  NB = 64 (two matrices per
-wavefront) serves fp64 and cfloat at orders 49..64 and fp32 Lower at 49..64;
-NB = 48 (24 lanes of a 32-lane group, two matrices per
-wavefront) fp64 and cfloat at 33..48 and fp32 at 35..48; NB = 128
-(one matrix per wavefront) fp32 Upper at 97..128; NB = 34 (17 lanes per
-matrix, three matrices per wavefront) fp32 Lower at 34.
+through LDS in slabs of whole (or half) cache lines.  NB = 64 (two matrices
+per wavefront) serves fp64 at 49..64, cfloat at 57..64 and fp32 Lower at
+49..64; NB = 56 (28 lanes of a 32-lane group, two matrices per wavefront)
+cfloat at 49..56; NB = 48 (24 lanes of a 32-lane group) fp64 and cfloat at
+33..48 and fp32 at 35..48; NB = 128 (one matrix per wavefront) fp32 Upper at
+97..128; NB = 34 (17 lanes per matrix, three matrices per wavefront) fp32
+Lower at 34; NB = 32 (16 lanes, four matrices per wavefront) cdouble Lower at
+17..32.
 
 Same bar as the other families: info bit-exact on every item, the referenced
 triangle within 1e-4 (cfloat) or 1e-11 (fp64) relative Frobenius error per
@@ -32,8 +34,9 @@ pytestmark = pytest.mark.gpu
 UPLOS = ["L", "U"]
 DTS = ["f64", "c64"]
 # (dtype, triangle, orders) served by the folded window
-ROUTES = [(dt, uplo, (33, 48, 49, 64)) for dt in DTS for uplo in UPLOS] + \
-         [("f32", "L", (34, 35, 48, 49, 64)), ("f32", "U", (35, 48, 97, 112, 128))]
+ROUTES = [(dt, uplo, (33, 48, 49, 56, 57, 64)) for dt in DTS for uplo in UPLOS] + \
+         [("f32", "L", (34, 35, 48, 49, 64)), ("f32", "U", (35, 48, 97, 112, 128)),
+          ("c128", "L", (17, 24, 32))]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -64,7 +67,7 @@ def test_fold_info_first_failure_nan_and_stale_pivot(dt, uplo, n):
     import dense_linear_algebra_potrf_amd as bl
     r = bl.route(dt, uplo, n, 9, family="tiny")
     h = r["lanes_per_matrix"]                 # NB / 2
-    assert h in (17, 24, 32, 64) and (r["rows_per_lane"], r["matrices_per_wave"]) == (2, 64 // h)
+    assert h in (16, 17, 24, 28, 32, 64) and (r["rows_per_lane"], r["matrices_per_wave"]) == (2, 64 // h)
     a = syn.spd_matrices(n, 9, dt, seed=71 + n)
     a[0, 3, 3] *= -1
     a[0, n - 2, n - 2] *= -1                  # two plants: the first wins
@@ -102,7 +105,7 @@ def test_fold_small_and_odd_batches(dt, uplo, orders):
 
 @pytest.mark.parametrize("dt,uplo,n", [("c64", "U", 33), ("c64", "L", 48), ("f64", "L", 33),
                                        ("f64", "U", 40), ("f32", "L", 40), ("f32", "U", 100),
-                                       ("f32", "L", 34)])
+                                       ("f32", "L", 34), ("c128", "L", 20), ("c64", "U", 52)])
 def test_fold_batch_beyond_the_grid_cap_is_uniform(dt, uplo, n):
     """More wavefronts of matrices than the launch's workgroups (2^19): every
     workgroup loops over several, and with two matrices per wavefront the odd
@@ -166,7 +169,8 @@ def test_fold_stride_beyond_a_pair_uses_the_one_wavefront_window(dt, uplo):
 @pytest.mark.parametrize("dt,uplo,n,batch", [("c64", "U", 64, 4096), ("c64", "L", 40, 2049),
                                               ("f64", "L", 48, 4096), ("f64", "U", 64, 2047),
                                               ("f32", "L", 64, 4095), ("f32", "U", 128, 2048),
-                                              ("f32", "L", 34, 16383)])
+                                              ("f32", "L", 34, 16383), ("c128", "L", 32, 2047),
+                                              ("c64", "U", 56, 4096)])
 def test_fold_batch_of_distinct_items_matches_the_oracle_at_every_item(dt, uplo, n, batch):
     """Thousands of distinct matrices (cfloat Upper n = 64: the secondary
     workload's shape): every item against the oracle, in chunks."""
