@@ -1,8 +1,8 @@
 // Tiny-family kernels for element type double (one translation unit per type so
-// the kernels build in parallel).  Orders 33..64 run in the folded window (two
-// matrices per wavefront, a short and a long row per lane), orders above the
-// register windows in the wide window (tiles over several wavefronts); both are
-// built in translation units of their own.
+// the kernels build in parallel).  Orders 25..64 run in the folded window (a
+// short and a long row per lane), orders above the register windows in the
+// wide window (tiles over several wavefronts); both are built in translation
+// units of their own.
 #include "tiny_impl.hpp"
 #include "wide_impl.hpp"
 #include "fold_impl.hpp"
@@ -18,12 +18,14 @@ hipError_t fold_potrf_f64(bool upper, int n, double* a, int64_t lda, int64_t str
 
 namespace {
 bool wide_order(int n) { return n > tiny_detail::last_nb(tiny_detail::TinyConfigs<double>::type{}); }
-// orders 33..64 in the folded window where a pair of matrices fits its 31-bit
-// offsets (else the one-wavefront window): up to 48 in the 48-row window
-// (1.23-1.39x the 64-row one on MI355X at b16384), the rest in the 64-row one
-// (a 56-row window, without DPP updates since 56 rows are not whole groups of
-// 16, measured 0.91-0.95x at 49..56)
+// orders 25..64 in the folded window where its wavefront's matrices fit the
+// 31-bit offsets (else the register windows): 25..32 in the 32-row window
+// (1.13-1.29x the 8 x 4 window on MI355X at b16384), 33..48 in the 48-row
+// window (1.23-1.39x the 64-row one), the rest in the 64-row one (a 56-row
+// window, without DPP updates since 56 rows are not whole groups of 16,
+// measured 0.91-0.95x at 49..56)
 bool use_fold(int n, int64_t stride) {
+    if (n >= 25 && n <= 32) return fold_detail::fold_layout_ok<double, 32>(stride);
     return n >= fold_detail::kFoldMin && n <= fold_detail::kFoldMax && fold_detail::fold_layout_ok<double, 64>(stride);
 }
 }  // namespace
@@ -43,7 +45,8 @@ bool tiny_geometry_f64(bool upper, int n, int64_t lda, int64_t stride, int64_t b
         return true;
     }
     if (use_fold(n, stride)) {
-        if (n <= 48) fold_detail::fold_geometry<double, 48>(upper, batch, g);
+        if (n <= 32) fold_detail::fold_geometry<double, 32>(upper, batch, g);
+        else if (n <= 48) fold_detail::fold_geometry<double, 48>(upper, batch, g);
         else fold_detail::fold_geometry<double, 64>(upper, batch, g);
         return true;
     }

@@ -284,6 +284,15 @@ def test_route_folded_window_geometry(lib):
         assert bl.route(dt, "L", 40, 4, stride=top - 1)["lanes_per_matrix"] == 24
         r = bl.route(dt, "L", 40, 4, stride=top + 64)
         assert r["family"] == "tiny" and r["lanes_per_matrix"] == 64 and r["matrices_per_wave"] == 1
+    # fp64 25..32: the 32-row window (16 lanes, four matrices per wavefront)
+    for uplo in ("L", "U"):
+        for n in (25, 28, 32):
+            r = bl.route("f64", uplo, n, 1001)
+            assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == (16, 2, 4)
+            assert r["grid"] == 251
+            assert r["lds_bytes"] == 2 * 4 * 36 * 8 + (4 * 32 * 17 * 8 if uplo == "U" else 0)
+    assert bl.route("f64", "L", 24, 1001)["lanes_per_matrix"] == 8
+    assert bl.route("c64", "L", 32, 1001)["lanes_per_matrix"] == 8
     # cdouble Lower 17..32: the 32-row window (16 lanes, four matrices per
     # wavefront); Upper keeps 32 x 1
     for n in (17, 24, 32):

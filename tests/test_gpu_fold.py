@@ -8,7 +8,7 @@ cfloat at 49..56; NB = 48 (24 lanes of a 32-lane group) fp64 and cfloat at
 33..48 and fp32 at 35..48; NB = 128 (one matrix per wavefront) fp32 Upper at
 97..128; NB = 34 (17 lanes per matrix, three matrices per wavefront) fp32
 Lower at 34; NB = 32 (16 lanes, four matrices per wavefront) cdouble Lower at
-17..32.
+17..32 and fp64 at 25..32.
 
 Same bar as the other families: info bit-exact on every item, the referenced
 triangle within 1e-4 (cfloat) or 1e-11 (fp64) relative Frobenius error per
@@ -34,7 +34,8 @@ pytestmark = pytest.mark.gpu
 UPLOS = ["L", "U"]
 DTS = ["f64", "c64"]
 # (dtype, triangle, orders) served by the folded window
-ROUTES = [(dt, uplo, (33, 48, 49, 56, 57, 64)) for dt in DTS for uplo in UPLOS] + \
+ROUTES = [("f64", uplo, (25, 32, 33, 48, 49, 56, 57, 64)) for uplo in UPLOS] + \
+         [("c64", uplo, (33, 48, 49, 56, 57, 64)) for uplo in UPLOS] + \
          [("f32", "L", (34, 35, 48, 49, 64)), ("f32", "U", (35, 48, 97, 112, 128)),
           ("c128", "L", (17, 24, 32))]
 
@@ -105,7 +106,8 @@ def test_fold_small_and_odd_batches(dt, uplo, orders):
 
 @pytest.mark.parametrize("dt,uplo,n", [("c64", "U", 33), ("c64", "L", 48), ("f64", "L", 33),
                                        ("f64", "U", 40), ("f32", "L", 40), ("f32", "U", 100),
-                                       ("f32", "L", 34), ("c128", "L", 20), ("c64", "U", 52)])
+                                       ("f32", "L", 34), ("c128", "L", 20), ("c64", "U", 52),
+                                       ("f64", "U", 28)])
 def test_fold_batch_beyond_the_grid_cap_is_uniform(dt, uplo, n):
     """More wavefronts of matrices than the launch's workgroups (2^19): every
     workgroup loops over several, and with two matrices per wavefront the odd
@@ -170,7 +172,7 @@ def test_fold_stride_beyond_a_pair_uses_the_one_wavefront_window(dt, uplo):
                                               ("f64", "L", 48, 4096), ("f64", "U", 64, 2047),
                                               ("f32", "L", 64, 4095), ("f32", "U", 128, 2048),
                                               ("f32", "L", 34, 16383), ("c128", "L", 32, 2047),
-                                              ("c64", "U", 56, 4096)])
+                                              ("c64", "U", 56, 4096), ("f64", "L", 32, 8191)])
 def test_fold_batch_of_distinct_items_matches_the_oracle_at_every_item(dt, uplo, n, batch):
     """Thousands of distinct matrices (cfloat Upper n = 64: the secondary
     workload's shape): every item against the oracle, in chunks."""
