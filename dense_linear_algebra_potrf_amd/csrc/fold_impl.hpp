@@ -48,9 +48,13 @@ template <int NB> constexpr int fold_groups() { return (64 + fold_gsize<NB>() - 
 // group, padding
 template <int NB> constexpr int fold_slot() { return NB + 2 * (fold_gsize<NB>() - NB / 2) + 4; }
 // rows of A in a slab: one 128-byte line of a column, or half a line where
-// whole lines do not divide the window (fp32 at 48 rows)
+// whole lines do not divide the window or its lane group (fp32 at 32 and 48
+// rows, 8-byte types at 56)
 template <typename T, int NB>
-constexpr int fold_slab_rows() { return NB % (128 / int(sizeof(T))) == 0 ? 128 / int(sizeof(T)) : 64 / int(sizeof(T)); }
+constexpr int fold_slab_rows() {
+    return NB % (128 / int(sizeof(T))) == 0 && fold_gsize<NB>() % (128 / int(sizeof(T))) == 0
+               ? 128 / int(sizeof(T)) : 64 / int(sizeof(T));
+}
 // occupancy asked of the compiler, from the registers a lane's values take:
 // up to 51 (the fp32 34-row window) six wavefronts per SIMD, up to 72 four,
 // more two (144 registers of values at three wavefronts spilled)

@@ -17,7 +17,8 @@ hipError_t fold_potrf_f32(bool upper, int n, float* a, int64_t lda, int64_t stri
 namespace {
 bool wide_order(int n) { return n > tiny_detail::last_nb(tiny_detail::TinyConfigs<float>::type{}); }
 // The folded window where it measured faster on MI355X (b16384, against the
-// window it replaces): Lower 34 in the 34-row window (1.6x the 64-row one;
+// window it replaces): Upper 25..32 in the 32-row window (1.03-1.35x the
+// 16 x 2 window; Lower there 0.83-0.88x), Lower 34 in the 34-row window (1.6x the 64-row one;
 // order 33 keeps its 11 x 3 window, 44.5 against 51.7 us), 35..48 in the
 // 48-row window (Lower 1.29-1.43x the 64-row one, Upper 1.52-1.76x the 64 x 1
 // window), Lower 49..64 in the 64-row window (1.06-1.23x the 64 x 1 window;
@@ -27,6 +28,7 @@ bool wide_order(int n) { return n > tiny_detail::last_nb(tiny_detail::TinyConfig
 // layout already skipping the triangle per wavefront), and only where a
 // wavefront's matrices fit the 31-bit offsets.
 bool use_fold(bool upper, int n, int64_t stride) {
+    if (upper && n >= 25 && n <= 32) return fold_detail::fold_layout_ok<float, 32>(stride);
     if (!upper && n == 34) return fold_detail::fold_layout_ok<float, 34>(stride);
     if (n >= 35 && n <= 48) return fold_detail::fold_layout_ok<float, 48>(stride);
     if (!upper && n >= 49 && n <= 64) return fold_detail::fold_layout_ok<float, 64>(stride);
@@ -44,7 +46,8 @@ bool tiny_layout_ok_f32(int n, int64_t stride) {
 
 bool tiny_geometry_f32(bool upper, int n, int64_t lda, int64_t stride, int64_t batch, Geometry& g) {
     if (use_fold(upper, n, stride)) {
-        if (n <= 34) fold_detail::fold_geometry<float, 34>(upper, batch, g);
+        if (n <= 32) fold_detail::fold_geometry<float, 32>(upper, batch, g);
+        else if (n <= 34) fold_detail::fold_geometry<float, 34>(upper, batch, g);
         else if (n <= 48) fold_detail::fold_geometry<float, 48>(upper, batch, g);
         else if (n <= 64) fold_detail::fold_geometry<float, 64>(upper, batch, g);
         else fold_detail::fold_geometry<float, 128>(upper, batch, g);

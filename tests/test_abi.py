@@ -292,6 +292,12 @@ def test_route_folded_window_geometry(lib):
             assert r["grid"] == 251
             assert r["lds_bytes"] == 2 * 4 * 36 * 8 + (4 * 32 * 17 * 8 if uplo == "U" else 0)
     assert bl.route("f64", "L", 24, 1001)["lanes_per_matrix"] == 8
+    for n in (25, 32):                    # fp32: Upper only (Lower keeps its 16 x 2 window)
+        r = bl.route("f32", "U", n, 1001)
+        assert (r["lanes_per_matrix"], r["rows_per_lane"], r["matrices_per_wave"]) == (16, 2, 4)
+        assert r["lds_bytes"] == 2 * 4 * 36 * 4 + 4 * 32 * 17 * 4
+        assert bl.route("f32", "L", n, 1001)["lanes_per_matrix"] == 16
+        assert bl.route("f32", "L", n, 1001)["matrices_per_wave"] == 4
     assert bl.route("c64", "L", 32, 1001)["lanes_per_matrix"] == 8
     # cdouble Lower 17..32: the 32-row window (16 lanes, four matrices per
     # wavefront); Upper keeps 32 x 1

@@ -8,7 +8,7 @@ cfloat at 49..56; NB = 48 (24 lanes of a 32-lane group) fp64 and cfloat at
 33..48 and fp32 at 35..48; NB = 128 (one matrix per wavefront) fp32 Upper at
 97..128; NB = 34 (17 lanes per matrix, three matrices per wavefront) fp32
 Lower at 34; NB = 32 (16 lanes, four matrices per wavefront) cdouble Lower at
-17..32 and fp64 at 25..32.
+17..32, fp64 at 25..32 and fp32 Upper at 25..32.
 
 Same bar as the other families: info bit-exact on every item, the referenced
 triangle within 1e-4 (cfloat) or 1e-11 (fp64) relative Frobenius error per
@@ -36,7 +36,7 @@ DTS = ["f64", "c64"]
 # (dtype, triangle, orders) served by the folded window
 ROUTES = [("f64", uplo, (25, 32, 33, 48, 49, 56, 57, 64)) for uplo in UPLOS] + \
          [("c64", uplo, (33, 48, 49, 56, 57, 64)) for uplo in UPLOS] + \
-         [("f32", "L", (34, 35, 48, 49, 64)), ("f32", "U", (35, 48, 97, 112, 128)),
+         [("f32", "L", (34, 35, 48, 49, 64)), ("f32", "U", (25, 32, 35, 48, 97, 112, 128)),
           ("c128", "L", (17, 24, 32))]
 
 
