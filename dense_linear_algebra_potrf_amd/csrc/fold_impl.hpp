@@ -92,11 +92,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(fold_waves_p
     // Upper: lane q's rows are columns of A, so loads and stores per row would
     // touch a cache line per lane and element.  The referenced triangle
     // instead moves in slabs of SR rows of A (SR elements = one 128-byte line
-    // of a column): each instruction covers whole lines (LPI columns per
-    // matrix), the slab is transposed through a tile of NB columns per matrix
-    // (a column's SR elements plus one element of padding), and every lane
-    // picks its two columns out of it.  A slab of the factor is written as
-    // soon as its SR columns are final.
+    // of a column, or half of one): each instruction covers whole lines (LPI
+    // columns per matrix), the slab is transposed through a tile of NB columns
+    // per matrix (a column's SR elements plus one element of padding; spare
+    // rows for idle lanes), and every lane picks its two columns out of it.
+    // A slab of the factor is written as soon as its SR columns are final.
     constexpr int SR = fold_slab_rows<T, NB>(), LPI = GS / SR > 0 ? GS / SR : 1, PITCH = SR + 1;
     constexpr int TR = fold_tile_rows<NB>();
     constexpr int GROUPS = fold_groups<NB>(), SLOT = fold_slot<NB>(), CB = 2 * GROUPS * SLOT;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(fold_waves_p
     const int lane = threadIdx.x & 63;
     const int h = lane / GS;                  // which matrix of the wavefront
     const int q = lane % GS;
-    const bool own = q < HALF;                // (the 48-row window's lanes 24..31 of a group are idle)
+    const bool own = q < HALF;                // (the 48- and 56-row windows' groups end in idle lanes)
     const int q16 = lane & 15;                // lane within its row of 16 (DPP broadcasts)
     const uint32_t lda_b = uint32_t(lda) * S;
 
