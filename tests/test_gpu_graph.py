@@ -15,7 +15,12 @@ pytestmark = pytest.mark.gpu
 
 CASES = [("f32", "L", 33, 4096, "tiny"), ("c64", "U", 64, 512, "tiny"),
          ("f32", "L", 128, 2048, "tiny"), ("c64", "U", 160, 256, "tiny"),
-         ("f32", "U", 48, 300, "lds"), ("f64", "L", 300, 40, "blocked")]
+         ("f32", "U", 48, 300, "lds"), ("f64", "L", 300, 40, "blocked"),
+         # the folded windows: 48 rows (odd batch), 128 rows (one matrix per
+         # wavefront), 32 rows (four), 34 rows (three), 56 rows
+         ("f64", "L", 40, 1001, "tiny"), ("f32", "U", 112, 513, "tiny"),
+         ("c128", "L", 24, 999, "tiny"), ("f32", "L", 34, 3001, "tiny"),
+         ("c64", "L", 52, 777, "tiny")]
 
 
 @pytest.mark.parametrize("dt,uplo,n,batch,family", CASES)
